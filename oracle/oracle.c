@@ -1,0 +1,402 @@
+/*
+ * oracle.c -- plain, slow, scalar CPU reference for group-wise RTN
+ * quantization, the W4A16 matmul that consumes its packed codes, and the
+ * SmoothQuant W8A8 path.
+ *
+ * THIS FILE IS TEST INFRASTRUCTURE. It is the independent checker for the
+ * HIP library: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it. The product path never calls it, and it shares
+ * no code, header, table or helper with the HIP sources.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * (no FMA contraction, IEEE single-precision division, round-half-to-even
+ * rintf under the default rounding mode, subnormals preserved).
+ *
+ * Sources (the five web pages on LLM post-training quantization):
+ *  [LP]  "3.6 Quantization" of the LLM learning path (liuzhe1218.github.io),
+ *        sections "Symmetric and asymmetric quantization", "Granularity",
+ *        "SmoothQuant", the PyTorch fake-quant code block and the worked
+ *        INT4 example.
+ *  [MK]  "Quantization: trading precision for performance in inference"
+ *        (mokono.cn), section 2.3 "core formulas" and 3.3/3.4 (sym/asym,
+ *        granularity).
+ *  [RL]  "LLM quantization deep dive" (rainlib.com), "Scale, Zero Point,
+ *        Group Size" and "granularity and matrix dimensions" (Y = X W^T,
+ *        W[out, in], groups along in_features).
+ *  [CP]  PTQ concept page (compassingai.com), "basic quantization formula"
+ *        and the SmoothQuant transform.
+ *  [CM]  Maths/CS/AI compendium ch.17 "Quantization" (godlockin.github.io),
+ *        "the quantization equation" and "activation quantization".
+ *
+ * Readings taken where the pages leave a step open (each is stated at the
+ * function that applies it):
+ *  - round() is round-half-to-even (the pages' executable code uses
+ *    torch.round / jnp.round);
+ *  - asymmetric codes round x/s first, then add z (every page writes
+ *    round(x/s) + z);
+ *  - range and absmax are floored at 1e-8 before the division ([LP] code);
+ *  - z is stored as an fp32 integer value, canonicalised to +0.0;
+ *  - symmetric codes lie in [-qmax, qmax], stored offset-binary (q + 8) for
+ *    INT4 and as signed int8 for INT8;
+ *  - INT4 packing is two codes per byte, low nibble = even input index
+ *    (the pages call the packing order implementation-defined);
+ *  - scales and zeros are fp32, layout [n][k / group];
+ *  - float results of the matmuls are fp64 sums of fp32 dequantized weights
+ *    times the bf16 activations.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#include <stdlib.h>
+
+#define ORACLE_FLOOR 1e-8f /* the pages' clamp(min=1e-8) on range / absmax */
+
+/* bf16 bits -> fp32: exact (bf16 is the top half of an fp32). */
+static float bf16_bits_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float clampf(float v, float lo, float hi)
+{
+    if (v < lo) return lo;
+    if (v > hi) return hi;
+    return v;
+}
+
+/* ------------------------------------------------------------------------
+ * One group of RTN quantization.
+ *
+ * [LP] "Symmetric and asymmetric quantization":
+ *   symmetric : qmax = 2^(b-1) - 1, s = max|x| / qmax,
+ *               q = clamp(round(x / s), -qmax, qmax), x_hat = s q
+ *   asymmetric: s = (max x - min x) / (2^b - 1), z = round(-min x / s),
+ *               q = clamp(round(x / s) + z, 0, 2^b - 1), x_hat = s (q - z)
+ * [LP] code block: range / absmax clamped to at least 1e-8 before dividing.
+ * Same formulas: [MK] 2.3 and 3.3, [CP] "basic quantization formula",
+ * [CM] "the quantization equation".
+ *
+ * x: the group's values in fp32 (already multiplied by col_scale when the
+ * caller applies SmoothQuant's weight-side scaling). Writes integer codes q
+ * (signed for symmetric, [0, 2^b-1] for asymmetric) and the group's s, z.
+ * ---------------------------------------------------------------------- */
+static void quantize_group(const float *x, int64_t g, int bits, int symmetric,
+                           int32_t *q, float *s_out, float *z_out)
+{
+    if (symmetric) {
+        const float qmax = (float)((1 << (bits - 1)) - 1); /* 7 or 127 */
+        float a = 0.0f;
+        for (int64_t j = 0; j < g; ++j) {
+            float v = fabsf(x[j]);
+            if (v > a) a = v;
+        }
+        if (a < ORACLE_FLOOR) a = ORACLE_FLOOR;
+        const float s = a / qmax;
+        for (int64_t j = 0; j < g; ++j) {
+            float r = rintf(x[j] / s);
+            q[j] = (int32_t)clampf(r, -qmax, qmax);
+        }
+        *s_out = s;
+        *z_out = 0.0f;
+    } else {
+        const float qmaxu = (float)((1 << bits) - 1); /* 15 or 255 */
+        float mn = x[0], mx = x[0];
+        for (int64_t j = 1; j < g; ++j) {
+            if (x[j] < mn) mn = x[j];
+            if (x[j] > mx) mx = x[j];
+        }
+        float range = mx - mn;
+        if (range < ORACLE_FLOOR) range = ORACLE_FLOOR;
+        const float s = range / qmaxu;
+        /* round(-min / s); "+ 0.0f" turns a -0.0 into +0.0 */
+        const float z = rintf(-mn / s) + 0.0f;
+        for (int64_t j = 0; j < g; ++j) {
+            float r = rintf(x[j] / s) + z; /* round first, then add z */
+            q[j] = (int32_t)clampf(r, 0.0f, qmaxu);
+        }
+        *s_out = s;
+        *z_out = z;
+    }
+}
+
+/* Storage of one code: INT4 symmetric is offset-binary q + 8 (0..15),
+ * INT4 asymmetric is q itself; INT8 symmetric is the int8 bit pattern,
+ * INT8 asymmetric is the uint8 value. */
+static void store_codes(const int32_t *q, int64_t k, int bits, int symmetric,
+                        uint8_t *row_codes)
+{
+    if (bits == 4) {
+        for (int64_t j = 0; j < k; j += 2) {
+            uint32_t u0 = (uint32_t)(symmetric ? q[j] + 8 : q[j]);
+            uint32_t u1 = (uint32_t)(symmetric ? q[j + 1] + 8 : q[j + 1]);
+            row_codes[j / 2] = (uint8_t)((u0 & 0xFu) | ((u1 & 0xFu) << 4));
+        }
+    } else {
+        for (int64_t j = 0; j < k; ++j)
+            row_codes[j] = (uint8_t)(symmetric ? (uint8_t)(int8_t)q[j] : (uint8_t)q[j]);
+    }
+}
+
+static int check_args(int64_t n, int64_t k, int bits, int64_t group)
+{
+    if (n < 0 || k <= 0 || group <= 0 || k % group != 0) return -1;
+    if (bits != 4 && bits != 8) return -1;
+    if (bits == 4 && (k % 2 != 0 || group % 2 != 0)) return -1;
+    return 0;
+}
+
+/* Quantize a row-major fp32 matrix w[n][k] group-wise along k (the input
+ * dimension; [RL] "granularity and matrix dimensions", [LP] "Granularity":
+ * per-group along the input dimension, G = 128 typical; group == k is
+ * per-channel, i.e. one scale per output row).
+ * col_scale (nullable, [k]): SmoothQuant's weight-side scaling, the row j of
+ * W (in Y = X W, [LP] "SmoothQuant") multiplied by s_j -- in the W[n][k]
+ * layout here, column k of w multiplied by col_scale[k] (fp32 product, not
+ * re-rounded) before the group statistics.
+ * codes: [n][k/2] (bits 4) or [n][k] (bits 8); scales, zeros: [n][k/group];
+ * zeros is written only for asymmetric. Returns 0, or -1 on bad arguments. */
+int oracle_quantize_f32(const float *w, int64_t n, int64_t k, int bits, int symmetric,
+                        int64_t group, const float *col_scale, uint8_t *codes,
+                        float *scales, float *zeros)
+{
+    if (check_args(n, k, bits, group)) return -1;
+    const int64_t ng = k / group;
+    const int64_t row_bytes = bits == 4 ? k / 2 : k;
+    float *x = (float *)malloc(sizeof(float) * (size_t)k);
+    int32_t *q = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    if (!x || !q) { free(x); free(q); return -1; }
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t j = 0; j < k; ++j) {
+            float v = w[r * k + j];
+            x[j] = col_scale ? v * col_scale[j] : v;
+        }
+        for (int64_t gi = 0; gi < ng; ++gi) {
+            float s, z;
+            quantize_group(x + gi * group, group, bits, symmetric, q + gi * group, &s, &z);
+            scales[r * ng + gi] = s;
+            if (!symmetric) zeros[r * ng + gi] = z;
+        }
+        store_codes(q, k, bits, symmetric, codes + r * row_bytes);
+    }
+    free(x);
+    free(q);
+    return 0;
+}
+
+/* Same, with the weights given as bf16 bit patterns (converted exactly). */
+int oracle_quantize_bf16(const uint16_t *w, int64_t n, int64_t k, int bits, int symmetric,
+                         int64_t group, const float *col_scale, uint8_t *codes,
+                         float *scales, float *zeros)
+{
+    if (check_args(n, k, bits, group)) return -1;
+    float *row = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!row) return -1;
+    const int64_t ng = k / group;
+    const int64_t row_bytes = bits == 4 ? k / 2 : k;
+    int rc = 0;
+    for (int64_t r = 0; r < n && rc == 0; ++r) {
+        for (int64_t j = 0; j < k; ++j) row[j] = bf16_bits_to_f32(w[r * k + j]);
+        rc = oracle_quantize_f32(row, 1, k, bits, symmetric, group, col_scale,
+                                 codes + r * row_bytes, scales + r * ng,
+                                 symmetric ? NULL : zeros + r * ng);
+    }
+    free(row);
+    return rc;
+}
+
+/* Integer code q of element j of a packed row: the asymmetric code itself,
+ * or the signed symmetric code (stored u - 8 for INT4, the int8 value for
+ * INT8), so that the dequantized value is (q - z) * s with z = 0 for
+ * symmetric. */
+static int32_t load_code(const uint8_t *row_codes, int64_t j, int bits, int symmetric)
+{
+    if (bits == 4) {
+        uint8_t b = row_codes[j / 2];
+        int32_t u = (j & 1) ? (b >> 4) : (b & 0xF);
+        return symmetric ? u - 8 : u;
+    }
+    return symmetric ? (int32_t)(int8_t)row_codes[j] : (int32_t)row_codes[j];
+}
+
+/* Dequantization, x_hat = s (q - z) ([LP] asymmetric equation; [MK] 2.3;
+ * [CM] "the quantization equation"), computed in fp32 as one rounding:
+ * fl((float)(q - z) * s). q - z is an exact small integer. out: [n][k]. */
+int oracle_dequantize(const uint8_t *codes, const float *scales, const float *zeros,
+                      int64_t n, int64_t k, int bits, int symmetric, int64_t group,
+                      float *out)
+{
+    if (check_args(n, k, bits, group)) return -1;
+    const int64_t ng = k / group;
+    const int64_t row_bytes = bits == 4 ? k / 2 : k;
+    for (int64_t r = 0; r < n; ++r) {
+        const uint8_t *rc = codes + r * row_bytes;
+        for (int64_t j = 0; j < k; ++j) {
+            const int64_t gi = j / group;
+            const float s = scales[r * ng + gi];
+            const float z = symmetric ? 0.0f : zeros[r * ng + gi];
+            const float qf = (float)load_code(rc, j, bits, symmetric);
+            out[r * k + j] = (qf - z) * s;
+        }
+    }
+    return 0;
+}
+
+/* W4A16 matmul ([RL] W4A16: INT4 weights, bf16 activations, weights
+ * dequantized and multiplied with the activations, higher-precision
+ * accumulation; [RL] linear layer Y = X W^T with W[out, in]):
+ *   y[i][r] = sum_j x[i][j] * x_hat[r][j]
+ * with x_hat the fp32 dequantized weights above, summed in fp64 in index
+ * order. x: bf16 bits [m][k]; y: fp64 [m][n]. */
+int oracle_w4a16_matmul(const uint16_t *x, int64_t m, const uint8_t *codes,
+                        const float *scales, const float *zeros, int64_t n, int64_t k,
+                        int symmetric, int64_t group, double *y)
+{
+    if (check_args(n, k, 4, group) || m < 0) return -1;
+    float *wrow = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!wrow) return -1;
+    const int64_t ng = k / group;
+    for (int64_t r = 0; r < n; ++r) {
+        oracle_dequantize(codes + r * (k / 2), scales + r * ng,
+                          symmetric ? NULL : zeros + r * ng, 1, k, 4, symmetric, group, wrow);
+        for (int64_t i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];
+            y[i * n + r] = acc;
+        }
+    }
+    free(wrow);
+    return 0;
+}
+
+/* SmoothQuant migration strength ([LP] "SmoothQuant"; [CP] SmoothQuant;
+ * [MK] SmoothQuant): s_j = max_t |X_tj|^alpha / max |W_j|^(1 - alpha).
+ * Input maxima are floored at 1e-8 (the pages' only floor constant; they
+ * are silent on an all-zero channel). alpha = 0.5 is taken as two
+ * correctly rounded square roots and one division; other alpha use powf. */
+void oracle_smooth_scale_from_absmax(const float *ax, const float *aw, int64_t k,
+                                     float alpha, float *s)
+{
+    for (int64_t j = 0; j < k; ++j) {
+        float a = ax[j] < ORACLE_FLOOR ? ORACLE_FLOOR : ax[j];
+        float b = aw[j] < ORACLE_FLOOR ? ORACLE_FLOOR : aw[j];
+        if (alpha == 0.5f)
+            s[j] = sqrtf(a) / sqrtf(b);
+        else
+            s[j] = powf(a, alpha) / powf(b, 1.0f - alpha);
+    }
+}
+
+/* Channel maxima: ax[j] = max over tokens of |X[t][j]|, aw[j] = max over
+ * output rows of |W[r][j]| (input channel j is a column of W[n][k]), then
+ * the migration strength above. x: bf16 [t][k]; w: bf16 [n][k]; s: [k]. */
+int oracle_smooth_scale(const uint16_t *x, int64_t t, const uint16_t *w, int64_t n,
+                        int64_t k, float alpha, float *s)
+{
+    if (t <= 0 || n <= 0 || k <= 0) return -1;
+    float *ax = (float *)calloc((size_t)k, sizeof(float));
+    float *aw = (float *)calloc((size_t)k, sizeof(float));
+    if (!ax || !aw) { free(ax); free(aw); return -1; }
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t j = 0; j < k; ++j) {
+            float v = fabsf(bf16_bits_to_f32(x[i * k + j]));
+            if (v > ax[j]) ax[j] = v;
+        }
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = 0; j < k; ++j) {
+            float v = fabsf(bf16_bits_to_f32(w[r * k + j]));
+            if (v > aw[j]) aw[j] = v;
+        }
+    oracle_smooth_scale_from_absmax(ax, aw, k, alpha, s);
+    free(ax);
+    free(aw);
+    return 0;
+}
+
+/* Dynamic per-token symmetric INT8 of the smoothed activations
+ * ([LP] "SmoothQuant": X diag(s)^-1, i.e. input channel j divided by s_j;
+ * [LP] code: quant_sym(X, 8, dim=1), one scale per token; [CM] "activation
+ * quantization": dynamic, per-token). X' = X / s in fp32 (not re-rounded),
+ * sx = max(max_j |X'_j|, 1e-8) / 127, qx = clamp(round(X' / sx), -127, 127).
+ * x: fp32 [t][k]; smooth nullable [k]; qx: [t][k]; sx: [t]. */
+int oracle_quant_per_token_int8_f32(const float *x, int64_t t, int64_t k,
+                                    const float *smooth, int8_t *qx, float *sx)
+{
+    if (t < 0 || k <= 0) return -1;
+    float *row = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!row) return -1;
+    for (int64_t i = 0; i < t; ++i) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float v = x[i * k + j];
+            row[j] = smooth ? v / smooth[j] : v;
+            float av = fabsf(row[j]);
+            if (av > a) a = av;
+        }
+        if (a < ORACLE_FLOOR) a = ORACLE_FLOOR;
+        const float s = a / 127.0f;
+        for (int64_t j = 0; j < k; ++j)
+            qx[i * k + j] = (int8_t)(int32_t)clampf(rintf(row[j] / s), -127.0f, 127.0f);
+        sx[i] = s;
+    }
+    free(row);
+    return 0;
+}
+
+/* Same with bf16 activations (converted exactly). */
+int oracle_quant_per_token_int8(const uint16_t *x, int64_t t, int64_t k,
+                                const float *smooth, int8_t *qx, float *sx)
+{
+    if (t < 0 || k <= 0) return -1;
+    float *row = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!row) return -1;
+    int rc = 0;
+    for (int64_t i = 0; i < t && rc == 0; ++i) {
+        for (int64_t j = 0; j < k; ++j) row[j] = bf16_bits_to_f32(x[i * k + j]);
+        rc = oracle_quant_per_token_int8_f32(row, 1, k, smooth, qx + i * k, sx + i);
+    }
+    free(row);
+    return rc;
+}
+
+/* W8A8 INT8 GEMM with INT32 accumulation and fp32 rescale ([CM] "activation
+ * quantization": INT8 weights and activations, INT32 accumulation; [LP]
+ * code: per-token activation scale times per-output-channel weight scale).
+ * acc[i][r] = sum_j qx[i][j] * qw[r][j] (exact int32 for |acc| < 2^31;
+ * the sum is formed in int64 and narrowed), y[i][r] = acc * sx[i] * sw[r]
+ * in fp64. acc nullable. */
+int oracle_w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *qw,
+                     const float *sw, int64_t n, int64_t k, int32_t *acc, double *y)
+{
+    if (m < 0 || n < 0 || k <= 0) return -1;
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t a = 0;
+            for (int64_t j = 0; j < k; ++j)
+                a += (int64_t)qx[i * k + j] * (int64_t)qw[r * k + j];
+            if (acc) acc[i * n + r] = (int32_t)a;
+            y[i * n + r] = (double)a * (double)sx[i] * (double)sw[r];
+        }
+    return 0;
+}
+
+/* Effective bits per weight ([MK] 3.4: 4 + 32/128 = 4.25 for a 16-bit scale
+ * and a 16-bit zero per 128 weights; [LP] "Granularity": 16/128 = 0.125 extra
+ * bits for a 16-bit scale; [LP] self-test: 4 + (16 + 4)/64 = 4.3125):
+ * metadata bits shared by a group are spread over its members. */
+double oracle_effective_bits(int bits, int scale_bits, int zero_bits, int64_t group)
+{
+    return (double)bits + (double)(scale_bits + zero_bits) / (double)group;
+}
+
+/* Bytes of the packed layout this library stores for an n x k matrix:
+ * codes + fp32 scales + fp32 zeros (asymmetric only). */
+int64_t oracle_packed_bytes(int64_t n, int64_t k, int bits, int symmetric, int64_t group)
+{
+    const int64_t codes = bits == 4 ? n * k / 2 : n * k;
+    const int64_t meta = n * (k / group) * 4 * (symmetric ? 1 : 2);
+    return codes + meta;
+}
