@@ -1,0 +1,233 @@
+"""bit_gemv_amd -- Python binding of libquant, the gfx950 C-ABI library.
+
+Argument marshalling only: every function takes torch tensors on the current
+HIP device, checks dtypes and shapes, allocates missing outputs with torch,
+and calls the C entry point of the same name (declared in
+``include/libquant.h``) on torch's current stream. All arithmetic happens in
+the HIP kernels of ``libquant.so``; there is no fallback. If the library is
+not built, importing the entry points raises.
+
+Layouts (see the header): W[n][k] row-major with groups of ``group`` along k;
+INT4 codes [n][k/2] (element 2j in the low nibble of byte j, symmetric codes
+stored as q + 8); INT8 codes [n][k]; fp32 scales and zeros [n][k/group].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libquant.so")
+
+LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = range(5)
+
+ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w4a16_gemm",
+                "smooth_scale", "quant_per_token_int8", "w8a8_gemm")
+
+
+class LibquantError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {detail} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libquant.so (torch is imported first, so its HIP runtime is the one
+    the library binds to). Raises if the library has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libquant.so not built ({p}); run `python -m bit_gemv_amd.build`")
+    lib = ctypes.CDLL(p)
+    P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sigs = {
+        "quantize_groupwise": [P, I64, I64, I, I, I64, P, P, P, P, P],
+        "dequantize_groupwise": [P, P, P, I64, I64, I, I, I64, P, P],
+        "w4a16_gemv": [P, I64, P, P, P, I64, I64, I, I64, P, P],
+        "w4a16_gemm": [P, I64, P, P, P, I64, I64, I, I64, P, P],
+        "smooth_scale": [P, I64, P, I64, I64, F, P, P],
+        "quant_per_token_int8": [P, I64, I64, P, P, P, P],
+        "w8a8_gemm": [P, P, I64, P, P, I64, I64, P, P, P],
+    }
+    for name, argtypes in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.lq_last_error.restype = ctypes.c_char_p
+    lib.lq_last_error.argtypes = []
+    lib.lq_status_string.restype = ctypes.c_char_p
+    lib.lq_status_string.argtypes = [ctypes.c_int]
+    lib.lq_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load_library()
+    st = getattr(lib, name)(*args)
+    if st != LQ_OK:
+        detail = lib.lq_last_error().decode() or lib.lq_status_string(st).decode()
+        raise LibquantError(st, name, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+@dataclass
+class PackedWeight:
+    """Output of quantize_groupwise: codes, scales, zeros plus their settings."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    zeros: Optional[torch.Tensor]
+    n: int
+    k: int
+    bits: int
+    symmetric: bool
+    group: int
+
+    def nbytes(self) -> int:
+        z = 0 if self.zeros is None else self.zeros.numel() * 4
+        return self.codes.numel() + self.scales.numel() * 4 + z
+
+
+def quantize_groupwise(w: torch.Tensor, bits: int = 4, symmetric: bool = False, group: int = 128,
+                       col_scale: Optional[torch.Tensor] = None, out: Optional[PackedWeight] = None
+                       ) -> PackedWeight:
+    """Group-wise RTN quantization of bf16 W[n][k] (see libquant.h)."""
+    n, k = w.shape
+    _need(w, "w", torch.bfloat16)
+    if col_scale is not None:
+        _need(col_scale, "col_scale", torch.float32, (k,))
+    if out is None:
+        dev = w.device
+        ng = k // group if group > 0 and k % group == 0 else 0
+        codes = torch.empty((n, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, ng), dtype=torch.float32, device=dev)
+        zeros = None if symmetric else torch.empty((n, ng), dtype=torch.float32, device=dev)
+        out = PackedWeight(codes, scales, zeros, n, k, bits, bool(symmetric), group)
+    _call("quantize_groupwise", _ptr(w), n, k, bits, int(bool(symmetric)), group, _ptr(col_scale),
+          _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _stream())
+    return out
+
+
+def dequantize_groupwise(pw: PackedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_hat = s (q - z) as fp32 [n][k]."""
+    if out is None:
+        out = torch.empty((pw.n, pw.k), dtype=torch.float32, device=pw.codes.device)
+    _need(out, "out", torch.float32, (pw.n, pw.k))
+    _call("dequantize_groupwise", _ptr(pw.codes), _ptr(pw.scales), _ptr(pw.zeros), pw.n, pw.k, pw.bits,
+          int(pw.symmetric), pw.group, _ptr(out), _stream())
+    return out
+
+
+def _w4(name: str, x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor]) -> torch.Tensor:
+    if pw.bits != 4:
+        raise ValueError(f"{name} needs INT4 codes")
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    if k != pw.k:
+        raise ValueError(f"x has {k} columns, weights have k = {pw.k}")
+    if y is None:
+        y = torch.empty((m, pw.n), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, pw.n))
+    _call(name, _ptr(x), m, _ptr(pw.codes), _ptr(pw.scales), _ptr(pw.zeros), pw.n, pw.k, int(pw.symmetric),
+          pw.group, _ptr(y), _stream())
+    return y
+
+
+def w4a16_gemv(x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[b][n] = x[b][k] W_hat^T for b <= 16 (fp32 out)."""
+    return _w4("w4a16_gemv", x, pw, y)
+
+
+def w4a16_gemm(x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[m][n] = x[m][k] W_hat^T for any m (fp32 out, bf16 MFMA)."""
+    return _w4("w4a16_gemm", x, pw, y)
+
+
+def smooth_scale(x: torch.Tensor, w: torch.Tensor, alpha: float = 0.5,
+                 s: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """s[k] = max_t|X[:,k]|^alpha / max_n|W[:,k]|^(1-alpha)."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    t, k = x.shape
+    n, kw = w.shape
+    if kw != k:
+        raise ValueError("x and w must share k")
+    if s is None:
+        s = torch.empty(k, dtype=torch.float32, device=x.device)
+    _need(s, "s", torch.float32, (k,))
+    _call("smooth_scale", _ptr(x), t, _ptr(w), n, k, float(alpha), _ptr(s), _stream())
+    return s
+
+
+def quant_per_token_int8(x: torch.Tensor, smooth: Optional[torch.Tensor] = None,
+                         qx: Optional[torch.Tensor] = None, sx: Optional[torch.Tensor] = None):
+    """Dynamic per-token symmetric INT8 of X / smooth -> (qx int8 [t][k], sx fp32 [t])."""
+    _need(x, "x", torch.bfloat16)
+    t, k = x.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, (k,))
+    if qx is None:
+        qx = torch.empty((t, k), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty(t, dtype=torch.float32, device=x.device)
+    _need(qx, "qx", torch.int8, (t, k))
+    _need(sx, "sx", torch.float32, (t,))
+    _call("quant_per_token_int8", _ptr(x), t, k, _ptr(smooth), _ptr(qx), _ptr(sx), _stream())
+    return qx, sx
+
+
+def w8a8_gemm(qx: torch.Tensor, sx: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+              y: Optional[torch.Tensor] = None, acc: Optional[torch.Tensor] = None, want_acc: bool = False):
+    """INT8 GEMM: acc = qx qw^T (int32), y = acc * sx * sw (fp32). Returns (y, acc or None)."""
+    _need(qx, "qx", torch.int8)
+    _need(qw, "qw", torch.int8)
+    m, k = qx.shape
+    n, kw = qw.shape
+    if kw != k:
+        raise ValueError("qx and qw must share k")
+    _need(sx, "sx", torch.float32, (m,))
+    _need(sw, "sw", torch.float32, (n,))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=qx.device)
+    if acc is None and want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=qx.device)
+    _need(y, "y", torch.float32, (m, n))
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (m, n))
+    _call("w8a8_gemm", _ptr(qx), _ptr(sx), m, _ptr(qw), _ptr(sw), n, k, _ptr(acc), _ptr(y), _stream())
+    return y, acc
+
+
+def abi_version() -> int:
+    return load_library().lq_abi_version()

@@ -1,0 +1,268 @@
+// api.cpp -- the extern "C" entry points of libquant (declared in
+// include/libquant.h): argument validation, then one launch on the caller's
+// stream. No allocation, no host<->device copies, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/libquant.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lq_status fail(lq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+// Device presence, checked once per process after a first success.
+std::atomic<int> g_have_device{0};
+
+lq_status need_device() {
+    if (g_have_device.load(std::memory_order_relaxed)) return LQ_OK;
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(LQ_ERR_NO_DEVICE, "no HIP device visible (%s)", hipGetErrorString(e));
+    }
+    g_have_device.store(1, std::memory_order_relaxed);
+    return LQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// Every output range must be disjoint from every input range and from the
+// other outputs.
+bool any_overlap(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Range &i : ins)
+            if (overlap(*o, i)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return true;
+    }
+    return false;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+lq_status launched(hipError_t e, const char *what) {
+    if (e == hipErrorNotSupported) return fail(LQ_ERR_UNSUPPORTED, "%s: not available in this build", what);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    }
+    g_err[0] = '\0';
+    return LQ_OK;
+}
+
+// Shared checks of the (bits, group, k) triple for quantize/dequantize.
+lq_status check_group(const char *fn, int64_t k, int bits, int64_t group) {
+    if (bits != 4 && bits != 8) return fail(LQ_ERR_INVALID_ARG, "%s: bits must be 4 or 8 (got %d)", fn, bits);
+    if (k <= 0 || group <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: k and group must be positive", fn);
+    if (k % group != 0) return fail(LQ_ERR_INVALID_ARG, "%s: k (%lld) is not a multiple of group (%lld)", fn,
+                                    (long long)k, (long long)group);
+    if (group % 128 != 0)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: group must be a multiple of 128 (got %lld)", fn, (long long)group);
+    if (k > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: k too large", fn);
+    return LQ_OK;
+}
+
+lq_status check_meta(const char *fn, int symmetric, const float *scales, const float *zeros) {
+    if (!scales || !aligned(scales, 4)) return fail(LQ_ERR_INVALID_ARG, "%s: scales null or misaligned", fn);
+    if (symmetric && zeros) return fail(LQ_ERR_INVALID_ARG, "%s: zeros must be NULL for symmetric", fn);
+    if (!symmetric && (!zeros || !aligned(zeros, 4)))
+        return fail(LQ_ERR_INVALID_ARG, "%s: zeros null or misaligned for asymmetric", fn);
+    return LQ_OK;
+}
+
+lq_status check_w4(const char *fn, const void *x, int64_t m, const void *codes, const float *scales,
+                   const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group, const float *y) {
+    if (m < 0 || n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size", fn);
+    lq_status st = check_group(fn, k, 4, group);
+    if (st != LQ_OK) return st;
+    if (n > kMaxDim || m > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    if (m == 0 || n == 0) return LQ_OK;
+    if (!x || !aligned(x, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (!y || !aligned(y, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: y null or not 16-byte aligned", fn);
+    st = check_meta(fn, symmetric, scales, zeros);
+    if (st != LQ_OK) return st;
+    const int64_t meta = n * (k / group) * 4;
+    if (any_overlap({{y, m * n * 4}},
+                    {{x, m * k * 2}, {codes, n * k / 2}, {scales, meta}, {zeros, symmetric ? 0 : meta}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    return LQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lq_abi_version(void) { return LQ_ABI_VERSION; }
+
+const char *lq_status_string(lq_status s) {
+    switch (s) {
+        case LQ_OK: return "ok";
+        case LQ_ERR_INVALID_ARG: return "invalid argument";
+        case LQ_ERR_UNSUPPORTED: return "unsupported";
+        case LQ_ERR_HIP: return "HIP error";
+        case LQ_ERR_NO_DEVICE: return "no device";
+    }
+    return "unknown status";
+}
+
+const char *lq_last_error(void) { return g_err; }
+
+lq_status quantize_groupwise(const void *w_bf16, int64_t n, int64_t k, int bits, int symmetric, int64_t group,
+                             const float *col_scale, void *codes, float *scales, float *zeros, void *stream) {
+    const char *fn = "quantize_groupwise";
+    if (n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative n", fn);
+    lq_status st = check_group(fn, k, bits, group);
+    if (st != LQ_OK) return st;
+    if (n > kMaxDim || n * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: matrix too large", fn);
+    if (n == 0) return LQ_OK;
+    if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (col_scale && !aligned(col_scale, 16))
+        return fail(LQ_ERR_INVALID_ARG, "%s: col_scale not 16-byte aligned", fn);
+    st = check_meta(fn, symmetric, scales, zeros);
+    if (st != LQ_OK) return st;
+    const int64_t meta = n * (k / group) * 4;
+    const int64_t cbytes = bits == 4 ? n * k / 2 : n * k;
+    if (any_overlap({{codes, cbytes}, {scales, meta}, {zeros, symmetric ? 0 : meta}},
+                    {{w_bf16, n * k * 2}, {col_scale, col_scale ? k * 4 : 0}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output overlaps an input or another output", fn);
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::QuantArgs a{static_cast<const uint16_t *>(w_bf16), n, k, bits, symmetric, group, col_scale,
+                    static_cast<uint8_t *>(codes), scales, zeros};
+    return launched(lq::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status dequantize_groupwise(const void *codes, const float *scales, const float *zeros, int64_t n, int64_t k,
+                               int bits, int symmetric, int64_t group, float *out, void *stream) {
+    const char *fn = "dequantize_groupwise";
+    if (n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative n", fn);
+    lq_status st = check_group(fn, k, bits, group);
+    if (st != LQ_OK) return st;
+    if (n > kMaxDim || n * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: matrix too large", fn);
+    if (n == 0) return LQ_OK;
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (!out || !aligned(out, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: out null or not 16-byte aligned", fn);
+    st = check_meta(fn, symmetric, scales, zeros);
+    if (st != LQ_OK) return st;
+    const int64_t meta = n * (k / group) * 4;
+    const int64_t cbytes = bits == 4 ? n * k / 2 : n * k;
+    if (any_overlap({{out, n * k * 4}}, {{codes, cbytes}, {scales, meta}, {zeros, symmetric ? 0 : meta}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::DequantArgs a{static_cast<const uint8_t *>(codes), scales, zeros, n, k, bits, symmetric, group, out};
+    return launched(lq::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales, const float *zeros,
+                     int64_t n, int64_t k, int symmetric, int64_t group, float *y, void *stream) {
+    const char *fn = "w4a16_gemv";
+    if (b > 16) return fail(LQ_ERR_UNSUPPORTED, "%s: batch %lld > 16 (use w4a16_gemm)", fn, (long long)b);
+    lq_status st = check_w4(fn, x_bf16, b, codes, scales, zeros, n, k, symmetric, group, y);
+    if (st != LQ_OK || b == 0 || n == 0) return st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::W4Args a{static_cast<const uint16_t *>(x_bf16), b, static_cast<const uint8_t *>(codes), scales, zeros,
+                 n, k, symmetric, group, y};
+    return launched(lq::launch_w4a16_gemv(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status w4a16_gemm(const void *x_bf16, int64_t m, const void *codes, const float *scales, const float *zeros,
+                     int64_t n, int64_t k, int symmetric, int64_t group, float *y, void *stream) {
+    const char *fn = "w4a16_gemm";
+    lq_status st = check_w4(fn, x_bf16, m, codes, scales, zeros, n, k, symmetric, group, y);
+    if (st != LQ_OK || m == 0 || n == 0) return st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::W4Args a{static_cast<const uint16_t *>(x_bf16), m, static_cast<const uint8_t *>(codes), scales, zeros,
+                 n, k, symmetric, group, y};
+    return launched(lq::launch_w4a16_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status smooth_scale(const void *x_bf16, int64_t t, const void *w_bf16, int64_t n, int64_t k, float alpha,
+                       float *s, void *stream) {
+    const char *fn = "smooth_scale";
+    if (t <= 0 || n <= 0 || k <= 0)
+        return fail(LQ_ERR_INVALID_ARG, "%s: t, n and k must be positive (channel maxima of empty tensors)", fn);
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(LQ_ERR_INVALID_ARG, "%s: alpha must be in [0, 1]", fn);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (t > kMaxDim || n > kMaxDim || k > kMaxDim || n * k > kMaxElems || t * k > kMaxElems)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
+    if (!s || !aligned(s, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: s null or not 16-byte aligned", fn);
+    if (any_overlap({{s, k * 4}}, {{x_bf16, t * k * 2}, {w_bf16, n * k * 2}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::SmoothArgs a{static_cast<const uint16_t *>(x_bf16), t, static_cast<const uint16_t *>(w_bf16), n, k, alpha, s};
+    return launched(lq::launch_smooth_scale(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status quant_per_token_int8(const void *x_bf16, int64_t t, int64_t k, const float *smooth, int8_t *qx,
+                               float *sx, void *stream) {
+    const char *fn = "quant_per_token_int8";
+    if (t < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t must be >= 0 and k > 0", fn);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (t > kMaxDim || k > kMaxDim || t * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    if (t == 0) return LQ_OK;
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (smooth && !aligned(smooth, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: smooth not 16-byte aligned", fn);
+    if (!qx || !aligned(qx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: qx null or not 16-byte aligned", fn);
+    if (!sx || !aligned(sx, 4)) return fail(LQ_ERR_INVALID_ARG, "%s: sx null or misaligned", fn);
+    if (any_overlap({{qx, t * k}, {sx, t * 4}}, {{x_bf16, t * k * 2}, {smooth, smooth ? k * 4 : 0}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output overlaps an input or another output", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::TokenQuantArgs a{static_cast<const uint16_t *>(x_bf16), t, k, smooth, qx, sx};
+    return launched(lq::launch_quant_per_token(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *qw, const float *sw, int64_t n,
+                    int64_t k, int32_t *acc, float *y, void *stream) {
+    const char *fn = "w8a8_gemm";
+    if (m < 0 || n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size or k <= 0", fn);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (k > 133120) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 133120 could overflow the int32 accumulator", fn);
+    if (m > kMaxDim || n > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    if (m == 0 || n == 0) return LQ_OK;
+    if (!qx || !aligned(qx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: qx null or not 16-byte aligned", fn);
+    if (!qw || !aligned(qw, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: qw null or not 16-byte aligned", fn);
+    if (!sx || !aligned(sx, 4) || !sw || !aligned(sw, 4))
+        return fail(LQ_ERR_INVALID_ARG, "%s: sx/sw null or misaligned", fn);
+    if (!y || !aligned(y, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: y null or not 16-byte aligned", fn);
+    if (acc && !aligned(acc, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: acc not 16-byte aligned", fn);
+    if (any_overlap({{y, m * n * 4}, {acc, acc ? m * n * 4 : 0}},
+                    {{qx, m * k}, {qw, n * k}, {sx, m * 4}, {sw, n * 4}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output overlaps an input or another output", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::W8Args a{qx, sx, m, qw, sw, n, k, acc, y};
+    return launched(lq::launch_w8a8_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// common.hpp -- small device helpers shared by the gfx950 kernels of libquant.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LQ_DEVICE __device__ __forceinline__
+
+namespace lq {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> fp32 (exact: bf16 is the upper half of an fp32).
+LQ_DEVICE float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+LQ_DEVICE float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// The pages' clamp(min = 1e-8) floor on a range or absmax before the division.
+constexpr float kFloor = 1e-8f;
+
+// Same comparison order as the definition: below lo -> lo, above hi -> hi.
+LQ_DEVICE float clamp_code(float v, float lo, float hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Butterfly sum / max over `width` lanes (width a power of two, <= 64).
+template <int WIDTH>
+LQ_DEVICE float team_sum(float v) {
+#pragma unroll
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, WIDTH);
+    return v;
+}
+template <int WIDTH>
+LQ_DEVICE float team_max(float v) {
+#pragma unroll
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WIDTH));
+    return v;
+}
+template <int WIDTH>
+LQ_DEVICE float team_min(float v) {
+#pragma unroll
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, WIDTH));
+    return v;
+}
+
+// v_dot2_f32_bf16: acc + a.lo * b.lo + a.hi * b.hi, with both pairs passed
+// as packed 32-bit words.
+LQ_DEVICE float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+}  // namespace lq

@@ -1,0 +1,75 @@
+// launch.hpp -- argument records passed from the C-ABI layer (api.cpp) to
+// the per-kernel launchers. Arguments are validated before they get here.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lq {
+
+struct QuantArgs {
+    const uint16_t *w;
+    int64_t n, k;
+    int bits, symmetric;
+    int64_t group;
+    const float *col_scale;
+    uint8_t *codes;
+    float *scales, *zeros;
+};
+
+struct DequantArgs {
+    const uint8_t *codes;
+    const float *scales, *zeros;
+    int64_t n, k;
+    int bits, symmetric;
+    int64_t group;
+    float *out;
+};
+
+struct W4Args {
+    const uint16_t *x;
+    int64_t m;  // batch (GEMV) or tokens (GEMM)
+    const uint8_t *codes;
+    const float *scales, *zeros;
+    int64_t n, k;
+    int symmetric;
+    int64_t group;
+    float *y;
+};
+
+struct SmoothArgs {
+    const uint16_t *x;
+    int64_t t;
+    const uint16_t *w;
+    int64_t n, k;
+    float alpha;
+    float *s;
+};
+
+struct TokenQuantArgs {
+    const uint16_t *x;
+    int64_t t, k;
+    const float *smooth;
+    int8_t *qx;
+    float *sx;
+};
+
+struct W8Args {
+    const int8_t *qx;
+    const float *sx;
+    int64_t m;
+    const int8_t *qw;
+    const float *sw;
+    int64_t n, k;
+    int32_t *acc;
+    float *y;
+};
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
+hipError_t launch_w4a16_gemv(const W4Args &a, hipStream_t st);
+hipError_t launch_w4a16_gemm(const W4Args &a, hipStream_t st);
+hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st);
+hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st);
+hipError_t launch_w8a8_gemm(const W8Args &a, hipStream_t st);
+
+}  // namespace lq

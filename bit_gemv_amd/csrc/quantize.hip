@@ -1,0 +1,290 @@
+// quantize.hip -- group-wise RTN quantize/pack and dequantize for gfx950.
+//
+// Definition: "3.6 Quantization" (LLM learning path), section "Symmetric and
+// asymmetric quantization" and its code block (1e-8 floor on range/absmax,
+// torch.round = round half to even); "Quantization: trading precision for
+// performance" (mokono.cn) 2.3: q = round(x / s) + z, x_hat = (q - z) s.
+//
+// Both passes stream HBM once. Every scale, zero and code is produced with
+// the same fp32 operations, in the same order, as the IEEE definition:
+// correctly rounded division (the HIP default), rintf = round half to even,
+// no FMA contraction (the library is built with -ffp-contract=off).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lq {
+
+// Statistics of one group, reduced over a team of lanes, then s and z.
+template <bool SYM>
+struct GroupStats {
+    float a;   // symmetric: running max |x|
+    float mn;  // asymmetric: running min
+    float mx;  // asymmetric: running max
+    LQ_DEVICE void init() {
+        a = 0.0f;
+        mn = __builtin_inff();
+        mx = -__builtin_inff();
+    }
+    LQ_DEVICE void add(float v) {
+        if (SYM) {
+            a = fmaxf(a, fabsf(v));
+        } else {
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+        }
+    }
+};
+
+template <int BITS, bool SYM>
+LQ_DEVICE void scale_zero(float a, float mn, float mx, float &s, float &z) {
+    if (SYM) {
+        const float qmax = (float)((1 << (BITS - 1)) - 1);
+        float am = a < kFloor ? kFloor : a;
+        s = am / qmax;
+        z = 0.0f;
+    } else {
+        const float levels = (float)((1 << BITS) - 1);
+        float range = mx - mn;
+        range = range < kFloor ? kFloor : range;
+        s = range / levels;
+        z = rintf(-mn / s) + 0.0f;  // "+ 0.0f": -0 -> +0
+    }
+}
+
+// Integer code of one element (before the INT4 symmetric +8 offset).
+template <int BITS, bool SYM>
+LQ_DEVICE int code_of(float x, float s, float z) {
+    if (SYM) {
+        const float qmax = (float)((1 << (BITS - 1)) - 1);
+        return (int)clamp_code(rintf(x / s), -qmax, qmax);
+    } else {
+        const float levels = (float)((1 << BITS) - 1);
+        float r = rintf(x / s) + z;  // round first, then add z
+        return (int)clamp_code(r, 0.0f, levels);
+    }
+}
+
+LQ_DEVICE void unpack8(const u32x4 v, float x[8]) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// NT: streaming (nontemporal) load for data read exactly once.
+template <bool CS, bool NT>
+LQ_DEVICE void load8(const uint16_t *__restrict__ w, const float *__restrict__ cs, int64_t elem,
+                     int64_t col, float x[8]) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(w + elem);
+    const u32x4 v = NT ? __builtin_nontemporal_load(p) : *p;
+    unpack8(v, x);
+    if (CS) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cs + col);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cs + col + 4);
+        x[0] = x[0] * c0.x; x[1] = x[1] * c0.y; x[2] = x[2] * c0.z; x[3] = x[3] * c0.w;
+        x[4] = x[4] * c1.x; x[5] = x[5] * c1.y; x[6] = x[6] * c1.z; x[7] = x[7] * c1.w;
+    }
+}
+
+// Codes of 8 consecutive elements -> packed storage.
+template <int BITS, bool SYM>
+LQ_DEVICE void store8(uint8_t *__restrict__ codes, int64_t elem, const int q[8]) {
+    if (BITS == 4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= (uint32_t)((SYM ? q[i] + 8 : q[i]) & 0xF) << (4 * i);
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(codes + elem / 2));
+    } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= (uint32_t)(q[i] & 0xFF) << (8 * i);
+            hi |= (uint32_t)(q[i + 4] & 0xFF) << (8 * i);
+        }
+        u32x2 v;
+        v.x = lo;
+        v.y = hi;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + elem));
+    }
+}
+
+// group == 128: a team of 16 lanes owns one group, 8 elements (16 bytes of
+// bf16) per lane. Groups tile the rows contiguously, so group index g covers
+// elements [128 g, 128 g + 128) of the flattened matrix and its scale sits at
+// scales[g].
+template <int BITS, bool SYM, bool CS>
+__global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restrict__ w,
+                                                          int64_t ngroups, int64_t k,
+                                                          const float *__restrict__ cs,
+                                                          uint8_t *__restrict__ codes,
+                                                          float *__restrict__ scales,
+                                                          float *__restrict__ zeros) {
+    const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int l = threadIdx.x & 15;
+    if (g >= ngroups) return;  // the whole 16-lane team leaves together
+    const int64_t elem = g * 128 + l * 8;
+    float x[8];
+    load8<CS, true>(w, cs, elem, CS ? elem % k : 0, x);
+    GroupStats<SYM> st;
+    st.init();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.add(x[i]);
+    float a = 0.f, mn = 0.f, mx = 0.f;
+    if (SYM) {
+        a = team_max<16>(st.a);
+    } else {
+        mn = team_min<16>(st.mn);
+        mx = team_max<16>(st.mx);
+    }
+    float s, z;
+    scale_zero<BITS, SYM>(a, mn, mx, s, z);
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = code_of<BITS, SYM>(x[i], s, z);
+    store8<BITS, SYM>(codes, elem, q);
+    if (l == 0) {
+        scales[g] = s;
+        if (!SYM) zeros[g] = z;
+    }
+}
+
+// Larger groups (any multiple of 128, including group == k): one 256-lane
+// block per group, two passes over the group (statistics, then codes; the
+// second pass hits L2).
+template <int BITS, bool SYM, bool CS>
+__global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restrict__ w, int64_t group,
+                                                         int64_t k, const float *__restrict__ cs,
+                                                         uint8_t *__restrict__ codes,
+                                                         float *__restrict__ scales,
+                                                         float *__restrict__ zeros) {
+    __shared__ float red[3][4];
+    const int64_t g = blockIdx.x;
+    const int64_t base = g * group;
+    const int t = threadIdx.x;
+    GroupStats<SYM> st;
+    st.init();
+    for (int64_t e = t * 8; e < group; e += 2048) {
+        float x[8];
+        load8<CS, false>(w, cs, base + e, CS ? (base + e) % k : 0, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.add(x[i]);
+    }
+    float a = 0.f, mn = 0.f, mx = 0.f;
+    if (SYM) {
+        a = team_max<64>(st.a);
+    } else {
+        mn = team_min<64>(st.mn);
+        mx = team_max<64>(st.mx);
+    }
+    const int wave = t >> 6;
+    if ((t & 63) == 0) {
+        red[0][wave] = a;
+        red[1][wave] = mn;
+        red[2][wave] = mx;
+    }
+    __syncthreads();
+    if (SYM) {
+        a = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    } else {
+        mn = fminf(fminf(red[1][0], red[1][1]), fminf(red[1][2], red[1][3]));
+        mx = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    }
+    float s, z;
+    scale_zero<BITS, SYM>(a, mn, mx, s, z);
+    for (int64_t e = t * 8; e < group; e += 2048) {
+        float x[8];
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(w + base + e);
+        unpack8(v, x);
+        if (CS) {
+            const int64_t col = (base + e) % k;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = x[i] * cs[col + i];
+        }
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = code_of<BITS, SYM>(x[i], s, z);
+        store8<BITS, SYM>(codes, base + e, q);
+    }
+    if (t == 0) {
+        scales[g] = s;
+        if (!SYM) zeros[g] = z;
+    }
+}
+
+// x_hat = (q - z) * s, 8 consecutive elements per lane.
+template <int BITS, bool SYM>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
+                                                       const float *__restrict__ scales,
+                                                       const float *__restrict__ zeros,
+                                                       int64_t total8, int64_t group,
+                                                       float *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total8) return;
+    const int64_t elem = i * 8;
+    const int64_t g = elem / group;  // groups tile the flattened matrix
+    const float s = scales[g];
+    const float z = SYM ? 0.0f : zeros[g];
+    int q[8];
+    if (BITS == 4) {
+        const uint32_t word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + elem / 2));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int u = (int)((word >> (4 * j)) & 0xF);
+            q[j] = SYM ? u - 8 : u;
+        }
+    } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(codes + elem));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b0 = (v.x >> (8 * j)) & 0xFF, b1 = (v.y >> (8 * j)) & 0xFF;
+            q[j] = SYM ? (int)(int8_t)b0 : (int)b0;
+            q[j + 4] = SYM ? (int)(int8_t)b1 : (int)b1;
+        }
+    }
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = ((float)q[j] - z) * s;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(out + elem);
+    __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, dst);
+    __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, dst + 1);
+}
+
+template <int BITS, bool SYM, bool CS>
+static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
+    const int64_t ngroups = a.n * (a.k / a.group);
+    if (a.group == 128) {
+        const int64_t blocks = (ngroups * 16 + 255) / 256;
+        hipLaunchKernelGGL((quant_g128_kernel<BITS, SYM, CS>), dim3((uint32_t)blocks), dim3(256), 0, st,
+                           a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    } else {
+        hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS>), dim3((uint32_t)ngroups), dim3(256), 0, st,
+                           a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t st) {
+    const bool cs = a.col_scale != nullptr;
+#define LQ_Q(B, S)                                                              \
+    if (a.bits == B && (a.symmetric != 0) == S)                                 \
+        return cs ? launch_quant_t<B, S, true>(a, st) : launch_quant_t<B, S, false>(a, st);
+    LQ_Q(4, true) LQ_Q(4, false) LQ_Q(8, true) LQ_Q(8, false)
+#undef LQ_Q
+    return hipErrorInvalidValue;
+}
+
+template <int BITS, bool SYM>
+static hipError_t launch_dequant_t(const DequantArgs &a, hipStream_t st) {
+    const int64_t total8 = a.n * a.k / 8;
+    const int64_t blocks = (total8 + 255) / 256;
+    hipLaunchKernelGGL((dequant_kernel<BITS, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st,
+                       a.codes, a.scales, a.zeros, total8, a.group, a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st) {
+    if (a.bits == 4) return a.symmetric ? launch_dequant_t<4, true>(a, st) : launch_dequant_t<4, false>(a, st);
+    return a.symmetric ? launch_dequant_t<8, true>(a, st) : launch_dequant_t<8, false>(a, st);
+}
+
+}  // namespace lq

@@ -1,0 +1,159 @@
+// smooth.hip -- SmoothQuant migration strength and dynamic per-token INT8.
+//
+// "3.6 Quantization" (LLM learning path), section "SmoothQuant": for
+// Y = X W with X[T][C_in], every positive s gives
+// Y = (X diag(s)^-1)(diag(s) W); the method picks
+// s_j = max_t |X_tj|^alpha / max |W_j|^(1 - alpha), where W_j is the weight
+// row that multiplies input channel j (a column of our W[n][k]). Its code
+// block then quantizes X / s per token and W * s per output channel to INT8.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lq {
+
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Column maxima of |W| over rows, folded into s[] with atomicMax on the
+// bit patterns (non-negative floats order like their bits, and max is exact
+// and order-free, so the result is deterministic).
+// Block: 256 lanes x 8 columns = 2048 columns, `rows` rows.
+__global__ __launch_bounds__(256) void colmax_kernel(const uint16_t *__restrict__ w, int64_t n, int64_t k,
+                                                      int rows, uint32_t *__restrict__ acc) {
+    const int64_t col = (int64_t)blockIdx.x * 2048 + threadIdx.x * 8;
+    if (col >= k) return;
+    const int64_t r0 = (int64_t)blockIdx.y * rows;
+    const int64_t r1 = r0 + rows < n ? r0 + rows : n;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int64_t r = r0;
+    for (; r + 4 <= r1; r += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w + (r + u) * k + col));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m[0] = fmaxf(m[0], fabsf(bf16_lo(v[u].x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v[u].x)));
+            m[2] = fmaxf(m[2], fabsf(bf16_lo(v[u].y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v[u].y)));
+            m[4] = fmaxf(m[4], fabsf(bf16_lo(v[u].z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v[u].z)));
+            m[6] = fmaxf(m[6], fabsf(bf16_lo(v[u].w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v[u].w)));
+        }
+    }
+    for (; r < r1; ++r) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(w + r * k + col);
+        m[0] = fmaxf(m[0], fabsf(bf16_lo(v.x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v.x)));
+        m[2] = fmaxf(m[2], fabsf(bf16_lo(v.y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v.y)));
+        m[4] = fmaxf(m[4], fabsf(bf16_lo(v.z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v.z)));
+        m[6] = fmaxf(m[6], fabsf(bf16_lo(v.w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v.w)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) atomicMax(acc + col + i, __float_as_uint(m[i]));
+}
+
+// Column maxima of |X| (128 columns per block: 16 lanes x 8 columns, 16 row
+// phases reduced through LDS), then s = f(ax, aw) with aw read from s[].
+__global__ __launch_bounds__(256) void smooth_finalize_kernel(const uint16_t *__restrict__ x, int64_t t,
+                                                               int64_t k, float alpha,
+                                                               float *__restrict__ s) {
+    __shared__ float red[16][129];
+    const int cl = threadIdx.x & 15, ph = threadIdx.x >> 4;
+    const int64_t col = (int64_t)blockIdx.x * 128 + cl * 8;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t r = ph; r < t; r += 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(x + r * k + col);
+        m[0] = fmaxf(m[0], fabsf(bf16_lo(v.x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v.x)));
+        m[2] = fmaxf(m[2], fabsf(bf16_lo(v.y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v.y)));
+        m[4] = fmaxf(m[4], fabsf(bf16_lo(v.z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v.z)));
+        m[6] = fmaxf(m[6], fabsf(bf16_lo(v.w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v.w)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[ph][cl * 8 + i] = m[i];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        float ax = red[0][threadIdx.x];
+        for (int p = 1; p < 16; ++p) ax = fmaxf(ax, red[p][threadIdx.x]);
+        const int64_t j = (int64_t)blockIdx.x * 128 + threadIdx.x;
+        float aw = s[j];  // the column max of |W| left by colmax_kernel
+        const float a = ax < kFloor ? kFloor : ax;
+        const float b = aw < kFloor ? kFloor : aw;
+        float r;
+        if (alpha == 0.5f)
+            r = sqrtf(a) / sqrtf(b);
+        else
+            r = powf(a, alpha) / powf(b, 1.0f - alpha);
+        s[j] = r;
+    }
+}
+
+hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st) {
+    uint32_t *acc = reinterpret_cast<uint32_t *>(a.s);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((uint32_t)((a.k + 255) / 256)), dim3(256), 0, st, acc, a.k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rows = 64;
+    dim3 grid((uint32_t)((a.k + 2047) / 2048), (uint32_t)((a.n + rows - 1) / rows));
+    hipLaunchKernelGGL(colmax_kernel, grid, dim3(256), 0, st, a.w, a.n, a.k, rows, acc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(smooth_finalize_kernel, dim3((uint32_t)(a.k / 128)), dim3(256), 0, st, a.x, a.t, a.k,
+                       a.alpha, a.s);
+    return hipGetLastError();
+}
+
+// Per-token INT8: one block per token, two passes over the row (the second
+// recomputes the same X / smooth quotient, from L2).
+template <bool SM>
+__global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t *__restrict__ x, int64_t k,
+                                                           const float *__restrict__ smooth,
+                                                           int8_t *__restrict__ qx, float *__restrict__ sx) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const uint16_t *xr = x + row * k;
+    float a = 0.0f;
+    for (int64_t e = threadIdx.x * 8; e < k; e += 2048) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr + e);
+        float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xs = SM ? f[i] / smooth[e + i] : f[i];
+            a = fmaxf(a, fabsf(xs));
+        }
+    }
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float am = a < kFloor ? kFloor : a;
+    const float s = am / 127.0f;
+    for (int64_t e = threadIdx.x * 8; e < k; e += 2048) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr + e);
+        float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xs = SM ? f[i] / smooth[e + i] : f[i];
+            const int q = (int)clamp_code(rintf(xs / s), -127.0f, 127.0f);
+            if (i < 4)
+                lo |= (uint32_t)(q & 0xFF) << (8 * i);
+            else
+                hi |= (uint32_t)(q & 0xFF) << (8 * (i - 4));
+        }
+        *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo, hi};
+    }
+    if (threadIdx.x == 0) sx[row] = s;
+}
+
+hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st) {
+    if (a.smooth)
+        hipLaunchKernelGGL(token_quant_kernel<true>, dim3((uint32_t)a.t), dim3(256), 0, st, a.x, a.k, a.smooth,
+                           a.qx, a.sx);
+    else
+        hipLaunchKernelGGL(token_quant_kernel<false>, dim3((uint32_t)a.t), dim3(256), 0, st, a.x, a.k, a.smooth,
+                           a.qx, a.sx);
+    return hipGetLastError();
+}
+
+}  // namespace lq

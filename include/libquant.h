@@ -1,0 +1,202 @@
+/*
+ * libquant.h -- C ABI of the MI355X (gfx950) library for group-wise
+ * round-to-nearest (RTN) quantization, the W4A16 GEMV/GEMM that consumes its
+ * packed codes, and the SmoothQuant W8A8 path.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor pointer is a DEVICE pointer on the current HIP
+ *           device, allocated and owned by the caller. The library never
+ *           allocates, frees or keeps tensor memory, and keeps no state
+ *           between calls except a thread-local error string.
+ * Layout.   Row-major, the last index contiguous. Weights are W[n][k] with
+ *           n = output features and k = input features; activations are
+ *           X[m][k]. This is the linear layer Y = X W^T with W[out, in] and
+ *           per-group parameters along in_features ("LLM quantization deep
+ *           dive", rainlib.com, "granularity and matrix dimensions").
+ *           bf16 tensors are passed as raw 16-bit patterns (void*).
+ *           Packed INT4 codes: [n][k/2] bytes, element 2j in the low nibble
+ *           of byte j and element 2j+1 in the high nibble. INT8 codes:
+ *           [n][k] bytes. scales / zeros: fp32 [n][k/group].
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *           stream) and the call returns after the launch. Synchronising
+ *           is the caller's business. Calls that overlap on one stream are
+ *           ordered; calls on different streams that write the same buffer
+ *           race.
+ * Errors.   Every entry point returns an lq_status. Arguments are checked
+ *           before any HIP call. A rejected call enqueues no work and writes
+ *           no output. Outputs may not overlap inputs. No exception crosses
+ *           the ABI, and the library never prints or exits.
+ *           LQ_ERR_INVALID_ARG   null required pointer, negative size, k not a
+ *                                multiple of group, zeros given for a
+ *                                symmetric call (or missing for an
+ *                                asymmetric one), misaligned pointer,
+ *                                overlapping input/output ranges.
+ *           LQ_ERR_UNSUPPORTED   a well-formed request this build does not
+ *                                implement (see each entry point).
+ *           LQ_ERR_NO_DEVICE     no HIP device is visible.
+ *           LQ_ERR_HIP           a HIP launch failed; lq_last_error() names it.
+ *           Empty work (n == 0 or m == 0 / t == 0 / b == 0) is a successful
+ *           no-op.
+ * Alignment. bf16, code, int8 and output tensors: 16 bytes. fp32 scale,
+ *           zero and vector arguments: 4 bytes.
+ * Numerics. Inputs must be finite. Codes, scales, zeros, INT8 codes, the
+ *           smoothing factors at alpha = 0.5 and the W8A8 int32 accumulators
+ *           are bit-exact against the IEEE-fp32 definitions below (correctly
+ *           rounded division and square root, round-half-to-even, no FMA
+ *           contraction, subnormals kept). Float matmul outputs are fp32
+ *           accumulations; they agree with an fp64 evaluation of the same
+ *           definition to relative L2 <= 1e-3 and max abs <= 1e-2 max|y|.
+ *           One group whose values are all equal and above ~1e29 in magnitude
+ *           makes x/s overflow fp32; such groups are outside the contract.
+ */
+#ifndef LIBQUANT_H
+#define LIBQUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LQ_OK = 0,
+    LQ_ERR_INVALID_ARG = 1,
+    LQ_ERR_UNSUPPORTED = 2,
+    LQ_ERR_HIP = 3,
+    LQ_ERR_NO_DEVICE = 4
+} lq_status;
+
+/* Version of this ABI (incremented on any incompatible change). */
+#define LQ_ABI_VERSION 1
+int lq_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *lq_status_string(lq_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). The string
+ * is owned by the library and valid until the next call on this thread. */
+const char *lq_last_error(void);
+
+/*
+ * quantize_groupwise -- group-wise RTN quantization of W[n][k] along k.
+ *
+ * Definition ("3.6 Quantization", LLM learning path, section "Symmetric and
+ * asymmetric quantization", and its PyTorch code block; same formulas in
+ * "Quantization: trading precision for performance", mokono.cn, 2.3/3.3):
+ * for each row and each run of `group` consecutive k (x = W, times
+ * col_scale[k] in fp32 when col_scale is given):
+ *   symmetric : qmax = 2^(bits-1) - 1, s = max(max|x|, 1e-8) / qmax,
+ *               q = clamp(round(x / s), -qmax, qmax)
+ *   asymmetric: s = max(max x - min x, 1e-8) / (2^bits - 1),
+ *               z = round(-min x / s) (as fp32, -0 stored as +0),
+ *               q = clamp(round(x / s) + z, 0, 2^bits - 1)
+ * round() is round-half-to-even of the correctly rounded fp32 quotient.
+ *
+ * w_bf16     [n][k] bf16 weights.
+ * bits       4 or 8.
+ * symmetric  nonzero for symmetric (no zero point).
+ * group      group size along k. Supported: any multiple of 128 that
+ *            divides k (128 is the usual G; group == k is per-channel, one
+ *            scale per output row). Other values: LQ_ERR_UNSUPPORTED.
+ * col_scale  nullable fp32 [k]: SmoothQuant's weight-side factor ("3.6
+ *            Quantization", section "SmoothQuant": the weight row of input
+ *            channel j is multiplied by s_j), applied before the statistics.
+ * codes      out. bits 4: [n][k/2] packed nibbles, symmetric codes stored as
+ *            q + 8. bits 8: [n][k], int8 q (symmetric) or uint8 q.
+ * scales     out fp32 [n][k/group].
+ * zeros      out fp32 [n][k/group] for asymmetric; must be NULL for symmetric.
+ * k must be a multiple of 128.
+ */
+lq_status quantize_groupwise(const void *w_bf16, int64_t n, int64_t k, int bits, int symmetric,
+                             int64_t group, const float *col_scale, void *codes, float *scales,
+                             float *zeros, void *stream);
+
+/*
+ * dequantize_groupwise -- x_hat = s (q - z), in fp32 with a single rounding
+ * ("3.6 Quantization", asymmetric equation; "Quantization: trading precision
+ * for performance" 2.3, dequantization). For symmetric codes z = 0 (INT4
+ * codes stored as q + 8 are decoded to q first).
+ * codes/scales/zeros as written by quantize_groupwise; out: fp32 [n][k].
+ * Same bits / group / k constraints as quantize_groupwise.
+ */
+lq_status dequantize_groupwise(const void *codes, const float *scales, const float *zeros,
+                               int64_t n, int64_t k, int bits, int symmetric, int64_t group,
+                               float *out, void *stream);
+
+/*
+ * w4a16_gemv -- batch-b decode product with INT4 weights
+ * ("LLM quantization deep dive", W4A16: 4-bit weights in memory, 16-bit
+ * activations, unpack/dequantize inside the kernel fused with the product,
+ * higher-precision accumulation; "3.6 Quantization", weight-only
+ * quantization of memory-bound decoding):
+ *   y[i][r] = sum_j x[i][j] * (q[r][j] - z[r][j/group]) * s[r][j/group]
+ * x_bf16  [b][k] bf16 activations, b in 0..16 (larger: LQ_ERR_UNSUPPORTED;
+ *         use w4a16_gemm).
+ * codes   [n][k/2] INT4 codes from quantize_groupwise(bits = 4).
+ * scales  fp32 [n][k/group]; zeros fp32 [n][k/group] or NULL if symmetric.
+ * y       out fp32 [b][n].
+ * group: multiple of 128 dividing k; k multiple of 128.
+ */
+lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales,
+                     const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,
+                     float *y, void *stream);
+
+/*
+ * w4a16_gemm -- prefill-shaped product with INT4 weights, same definition
+ * as w4a16_gemv for any m ("LLM quantization deep dive", prefill is
+ * compute-bound; "3.6 Quantization", W4A16 does not speed up prefill).
+ * Runs on bf16 MFMA with exact integer weight operands and the per-group
+ * scale applied in fp32.
+ * x_bf16 [m][k]; y out fp32 [m][n]. Other arguments as w4a16_gemv.
+ */
+lq_status w4a16_gemm(const void *x_bf16, int64_t m, const void *codes, const float *scales,
+                     const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,
+                     float *y, void *stream);
+
+/*
+ * smooth_scale -- SmoothQuant migration strength ("3.6 Quantization",
+ * section "SmoothQuant"; PTQ concept page, SmoothQuant):
+ *   s[j] = max_t |X[t][j]|^alpha / max_r |W[r][j]|^(1 - alpha)
+ * with both maxima floored at 1e-8; alpha = 0.5 is evaluated as
+ * sqrt(ax) / sqrt(aw) (bit-exact), other alpha with powf (within 1e-6
+ * relative).
+ * x_bf16 [t][k] calibration activations; w_bf16 [n][k] weights; s out fp32
+ * [k]. alpha in [0, 1]. k multiple of 128. The output buffer s is also the
+ * kernels' running-maximum workspace while the call runs.
+ */
+lq_status smooth_scale(const void *x_bf16, int64_t t, const void *w_bf16, int64_t n, int64_t k,
+                       float alpha, float *s, void *stream);
+
+/*
+ * quant_per_token_int8 -- dynamic per-token symmetric INT8 of the smoothed
+ * activations ("3.6 Quantization", SmoothQuant section and code block:
+ * X diag(s)^-1, then one scale per token; compendium "Quantization",
+ * activation quantization: dynamic per-token):
+ *   X'[t][j] = X[t][j] / smooth[j] (fp32, not re-rounded; smooth may be
+ *   NULL for no smoothing), sx[t] = max(max_j |X'[t][j]|, 1e-8) / 127,
+ *   qx[t][j] = clamp(round(X'[t][j] / sx[t]), -127, 127).
+ * x_bf16 [t][k]; qx out int8 [t][k]; sx out fp32 [t]. k multiple of 128.
+ */
+lq_status quant_per_token_int8(const void *x_bf16, int64_t t, int64_t k, const float *smooth,
+                               int8_t *qx, float *sx, void *stream);
+
+/*
+ * w8a8_gemm -- INT8 x INT8 GEMM with INT32 accumulation and fp32 rescale
+ * (compendium "Quantization", activation quantization: INT8 operands,
+ * INT32 accumulation; "3.6 Quantization" code block: per-token activation
+ * scale times per-output-channel weight scale):
+ *   acc[i][r] = sum_j qx[i][j] * qw[r][j]   (exact; |acc| < 2^31 requires
+ *                                           k * 127^2 < 2^31, k <= 133144)
+ *   y[i][r]   = (acc[i][r] * sx[i]) * sw[r] in fp32.
+ * qx [m][k], qw [n][k] int8; sx fp32 [m]; sw fp32 [n]; acc out int32 [m][n]
+ * (nullable); y out fp32 [m][n]. k multiple of 128 and <= 133120.
+ */
+lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *qw,
+                    const float *sw, int64_t n, int64_t k, int32_t *acc, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBQUANT_H */

@@ -1,0 +1,123 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call.
+
+No compute call runs here. Calls with valid arguments are made only when no
+GPU is visible, where they must report LQ_ERR_NO_DEVICE without launching.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_gemv_amd as bg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libquant.h")
+
+P = ctypes.c_void_p
+A16 = P(1 << 20)          # a 16-byte-aligned fake address (never dereferenced)
+B16 = P(2 << 20)
+C16 = P(3 << 20)
+D16 = P(4 << 20)
+MIS = P((5 << 20) + 2)    # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bg.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:lq_status|const char \*|int)\s*\*?\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for ep in bg.ENTRY_POINTS:
+        assert ep in names
+    assert {"lq_status_string", "lq_last_error", "lq_abi_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_dynamic_symbols_are_exactly_c_names():
+    out = os.popen(f"nm -D --defined-only {bg.LIB_PATH}").read()
+    syms = set(re.findall(r" T (\w+)$", out, re.M))
+    for name in _declared_functions():
+        assert name in syms, name
+
+
+def test_status_strings(lib):
+    assert lib.lq_abi_version() == 1
+    assert lib.lq_status_string(0) == b"ok"
+    assert lib.lq_status_string(1) == b"invalid argument"
+    assert lib.lq_status_string(2) == b"unsupported"
+    assert lib.lq_status_string(4) == b"no device"
+
+
+def _q(lib, w=A16, n=4, k=256, bits=4, sym=0, group=128, cs=None, codes=B16, scales=C16, zeros=D16):
+    return lib.quantize_groupwise(w, n, k, bits, sym, group, cs, codes, scales, zeros, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(bits=5), 1),
+    (dict(bits=2), 1),
+    (dict(k=300, group=128), 1),              # k not a multiple of group
+    (dict(group=0), 1),
+    (dict(n=-1), 1),
+    (dict(k=0), 1),
+    (dict(group=64, k=256), 2),               # not a multiple of 128: unsupported
+    (dict(w=None), 1),
+    (dict(w=MIS), 1),
+    (dict(codes=MIS), 1),
+    (dict(sym=1), 1),                          # zeros given for symmetric
+    (dict(zeros=None), 1),                     # zeros missing for asymmetric
+    (dict(cs=P((6 << 20) + 4)), 1),            # col_scale not 16-byte aligned
+    (dict(codes=P((1 << 20) + 64)), 1),        # codes overlap w
+    (dict(scales=D16, zeros=D16), 1),          # two outputs overlap
+])
+def test_quantize_rejects(lib, kwargs, status):
+    assert _q(lib, **kwargs) == status
+    assert lib.lq_last_error() != b""
+
+
+def test_empty_work_is_ok(lib):
+    assert _q(lib, w=None, n=0, codes=None, scales=None, zeros=None) == 0
+    assert lib.w4a16_gemv(None, 0, None, None, None, 8, 256, 1, 128, None, None) == 0
+    assert lib.w4a16_gemm(None, 5, None, None, None, 0, 256, 1, 128, None, None) == 0
+    assert lib.quant_per_token_int8(None, 0, 256, None, None, None, None) == 0
+    assert lib.w8a8_gemm(None, None, 0, None, None, 4, 256, None, None, None) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A16, 17, B16, C16, None, 8, 256, 1, 128, D16), 2),   # batch > 16
+    ((A16, -1, B16, C16, None, 8, 256, 1, 128, D16), 1),
+    ((A16, 1, B16, C16, D16, 8, 256, 1, 128, P(5 << 20)), 1),  # zeros for symmetric
+    ((A16, 1, B16, C16, None, 8, 256, 0, 128, D16), 1),       # zeros missing
+    ((MIS, 1, B16, C16, None, 8, 256, 1, 128, D16), 1),
+    ((A16, 1, B16, C16, None, 8, 200, 1, 100, D16), 2),       # group not a multiple of 128
+    ((A16, 1, B16, C16, None, 8, 256, 1, 128, A16), 1),       # y aliases x
+])
+def test_gemv_rejects(lib, args, status):
+    assert lib.w4a16_gemv(*args, None) == status
+
+
+def test_smoothquant_entry_points_reject(lib):
+    assert lib.smooth_scale(A16, 0, B16, 8, 256, ctypes.c_float(0.5), C16, None) == 1
+    assert lib.smooth_scale(A16, 8, B16, 8, 256, ctypes.c_float(1.5), C16, None) == 1
+    assert lib.smooth_scale(A16, 8, B16, 8, 200, ctypes.c_float(0.5), C16, None) == 2
+    assert lib.quant_per_token_int8(A16, 4, 256, P((7 << 20) + 8), B16, C16, None) == 1
+    assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 256 * 1024, None, P(9 << 20), None) == 2
+    assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 256, P(9 << 20), P(9 << 20), None) == 1
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_valid_call_without_device_reports_no_device(lib):
+    assert _q(lib) == 4
+    assert b"no HIP device" in lib.lq_last_error()

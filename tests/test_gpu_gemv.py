@@ -1,0 +1,79 @@
+"""W4A16 GEMV (batch 1..16) against the oracle's fp64 result on the same codes."""
+import numpy as np
+import pytest
+
+import bit_gemv_amd as bg
+import oracle
+from gpu_helpers import assert_close, assert_same_bits, dev_bf16, host, say
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(n, k, b, sym, group=128, seed=0, w_scale=0.02, x_mult=None):
+    rng = np.random.default_rng(seed)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * w_scale)
+    xf = rng.standard_normal((b, k))
+    if x_mult is not None:
+        xf = xf * x_mult
+    x = f32_to_bf16_bits(xf)
+    say(f"gemv n={n} k={k} b={b} sym={sym} group={group}")
+    pw = bg.quantize_groupwise(dev_bf16(w), 4, sym, group)
+    c_ref, s_ref, z_ref = oracle.quantize(w, 4, sym, group)
+    assert_same_bits(host(pw.codes), c_ref, "codes")
+    y = host(bg.w4a16_gemv(dev_bf16(x), pw))
+    y_ref = oracle.w4a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, group)
+    assert_close(y, y_ref, f"y n={n} k={k} b={b}")
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(1, 128), (5, 384), (67, 2048 + 128), (300, 4096), (129, 11008),
+                                 (96, 8192), (33, 28672)])
+def test_batch1_shapes(n, k, sym):
+    _case(n, k, 1, sym)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 7, 8, 11, 16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_batches(b, sym):
+    _case(203, 4096 + 640, b, sym, seed=b)
+
+
+@pytest.mark.parametrize("group", [256, "k"])
+def test_larger_groups(group):
+    k = 2048
+    _case(77, k, 3, False, group=k if group == "k" else group)
+
+
+def test_activation_outlier_channels():
+    k = 4096
+    mult = np.ones(k)
+    mult[[5, 900, 4000]] = [20.0, 40.0, 60.0]
+    _case(128, k, 4, False, x_mult=mult, seed=3)
+
+
+def test_full_4096_square_batch1_asym():
+    """The 4096 x 4096 asymmetric INT4 single-matrix workload, every output."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS["single_4096"]
+    w = wl.weight(0, 0)
+    x = wl.activation(4096, 1)
+    say("gemv single_4096 full")
+    pw = bg.quantize_groupwise(dev_bf16(w), 4, False, 128)
+    c_ref, s_ref, z_ref = oracle.quantize(w, 4, False, 128)
+    assert_same_bits(host(pw.codes), c_ref, "codes")
+    assert_same_bits(host(pw.scales), s_ref, "scales")
+    assert_same_bits(host(pw.zeros), z_ref, "zeros")
+    y = host(bg.w4a16_gemv(dev_bf16(x), pw))
+    y_ref = oracle.w4a16_matmul(x, c_ref, s_ref, z_ref, 4096, 4096, False, 128)
+    assert_close(y, y_ref, "single_4096 y")
+
+
+def test_batch_over_16_is_unsupported():
+    import torch
+    w = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    pw = bg.quantize_groupwise(w, 4, True, 128)
+    x = torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bg.LibquantError) as e:
+        bg.w4a16_gemv(x, pw)
+    assert e.value.status == bg.LQ_ERR_UNSUPPORTED

@@ -1,0 +1,84 @@
+"""SmoothQuant path: smoothing scale, per-token INT8 and per-channel INT8
+weights, bit-exact against the oracle."""
+import numpy as np
+import pytest
+
+import bit_gemv_amd as bg
+import oracle
+from gpu_helpers import assert_same_bits, dev, dev_bf16, host, say
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _xw(t, n, k, seed=0, outliers=6, mult=50.0):
+    rng = np.random.default_rng(seed)
+    xf = rng.standard_normal((t, k))
+    idx = rng.choice(k, outliers, replace=False)
+    xf[:, idx] *= mult
+    wf = rng.standard_normal((n, k)) * 0.02
+    return f32_to_bf16_bits(xf), f32_to_bf16_bits(wf)
+
+
+@pytest.mark.parametrize("t,n,k", [(1, 1, 128), (7, 65, 384), (64, 300, 2048 + 128), (512, 1024, 8192)])
+def test_smooth_scale_alpha_half(t, n, k):
+    x, w = _xw(t, n, k, seed=t)
+    say(f"smooth_scale t={t} n={n} k={k}")
+    s = host(bg.smooth_scale(dev_bf16(x), dev_bf16(w), 0.5))
+    assert_same_bits(s, oracle.smooth_scale(x, w, 0.5), "s")
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.25, 0.8, 1.0])
+def test_smooth_scale_other_alpha(alpha):
+    x, w = _xw(33, 70, 1024, seed=2)
+    say(f"smooth_scale alpha={alpha}")
+    s = host(bg.smooth_scale(dev_bf16(x), dev_bf16(w), alpha))
+    ref = oracle.smooth_scale(x, w, alpha)
+    assert np.allclose(s, ref, rtol=1e-6, atol=0), np.abs(s / ref - 1).max()
+
+
+def test_smooth_scale_zero_channels():
+    x, w = _xw(8, 16, 256, seed=3)
+    x[:, 10] = 0
+    w[:, 11] = 0
+    x[:, 12] = 0
+    w[:, 12] = 0
+    say("smooth_scale zero channels")
+    s = host(bg.smooth_scale(dev_bf16(x), dev_bf16(w), 0.5))
+    assert_same_bits(s, oracle.smooth_scale(x, w, 0.5), "s")
+
+
+@pytest.mark.parametrize("smooth", [False, True])
+@pytest.mark.parametrize("t,k", [(1, 128), (5, 384), (64, 2048 + 128), (512, 8192)])
+def test_per_token_int8(t, k, smooth):
+    x, w = _xw(t, 16, k, seed=k)
+    sm = np.exp(np.random.default_rng(1).uniform(-2, 2, k)).astype(np.float32) if smooth else None
+    say(f"quant_per_token_int8 t={t} k={k} smooth={smooth}")
+    qx, sx = bg.quant_per_token_int8(dev_bf16(x), None if sm is None else dev(sm))
+    q_ref, s_ref = oracle.quant_per_token_int8(x, sm)
+    assert_same_bits(host(qx), q_ref, "qx")
+    assert_same_bits(host(sx), s_ref, "sx")
+
+
+def test_per_token_edge_rows():
+    k = 256
+    rows = [np.zeros(k), np.full(k, 2.5), np.linspace(-127, 127, k), np.full(k, 1e-39)]
+    x = f32_to_bf16_bits(np.stack(rows))
+    say("quant_per_token_int8 edge rows")
+    qx, sx = bg.quant_per_token_int8(dev_bf16(x))
+    q_ref, s_ref = oracle.quant_per_token_int8(x)
+    assert_same_bits(host(qx), q_ref, "qx")
+    assert_same_bits(host(sx), s_ref, "sx")
+
+
+def test_smoothed_weight_quantization_chain():
+    """s from the GPU, then W * s per-channel INT8 on both sides."""
+    x, w = _xw(128, 256, 4096, seed=11)
+    say("smoothquant weight chain")
+    s_gpu = bg.smooth_scale(dev_bf16(x), dev_bf16(w), 0.5)
+    s = host(s_gpu)
+    assert_same_bits(s, oracle.smooth_scale(x, w, 0.5), "s")
+    pw = bg.quantize_groupwise(dev_bf16(w), 8, True, 4096, s_gpu)
+    c_ref, sw_ref, _ = oracle.quantize(w, 8, True, 4096, s)
+    assert_same_bits(host(pw.codes), c_ref, "qw")
+    assert_same_bits(host(pw.scales), sw_ref, "sw")
