@@ -102,6 +102,8 @@ lq_status check_w4(const char *fn, const void *x, int64_t m, const void *codes, 
     lq_status st = check_group(fn, k, 4, group);
     if (st != LQ_OK) return st;
     if (n > kMaxDim || m > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    // kernels address a few rows of codes with 32-bit buffer offsets
+    if (k > (int64_t(1) << 28)) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 2^28", fn);
     if (m == 0 || n == 0) return LQ_OK;
     if (!x || !aligned(x, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
     if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);

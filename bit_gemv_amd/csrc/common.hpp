@@ -44,6 +44,14 @@ LQ_DEVICE float team_min(float v) {
     return v;
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3).
+// Loads whose offset falls outside return zeros instead of faulting.
+LQ_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any resource used here
+constexpr int kNonTemporal = 2;                // buffer-load cache policy: streaming
+
 // v_dot2_f32_bf16: acc + a.lo * b.lo + a.hi * b.hi, with both pairs passed
 // as packed 32-bit words.
 LQ_DEVICE float dot2_bf16(uint32_t a, uint32_t b, float acc) {

@@ -1,30 +1,26 @@
-// gemv.hip -- W4A16 decode GEMV on gfx950 VALU (v_dot2_f32_bf16).
+// gemv.hip -- W4A16 decode GEMV for gfx950: a VALU (v_dot2_f32_bf16) kernel
+// for batch 1..4 and an MFMA (16x16x32 bf16) kernel for batch 5..16.
 //
 // Definition ("LLM quantization deep dive", rainlib.com, W4A16: INT4 weights
 // in memory, unpacked and dequantized inside the kernel and multiplied with
 // 16-bit activations, higher-precision accumulation):
 //   y[b][r] = sum_j x[b][j] * (q[r][j] - z[r][j/G]) * s[r][j/G].
-// At batch 1-16 the product is bound by the bytes of codes and scales
+// At small batch the product is bound by the bytes of codes and scales
 // streamed from HBM ("3.6 Quantization": batch-1 decode time is bytes read
-// over bandwidth), so the kernel is built around one coalesced 16-byte code
-// load per lane and a small VALU budget per weight:
+// over bandwidth), so both kernels are built around coalesced 16-byte code
+// loads kept in flight and a small VALU budget per weight:
 //
 //  * A nibble c ORed into the mantissa of the bf16 0x4300 (= 128) gives the
 //    bf16 value 128 + c exactly, so one v_and_or_b32 turns two nibbles of a
-//    code word into a packed bf16 pair, and one v_dot2_f32_bf16 multiplies
-//    that pair with a pair of activations (exact products, fp32 sums).
-//  * The offset and the zero point are folded into a per-segment correction:
-//    sum x (q - z) s = s * (sum x (128 + q) - (128 + z) * sum x), where the
-//    activation sum comes from the same dot2 unit with a (1, 1) pair.
-//  * Nibbles 0..3 of a code word pair with nibbles 4..7, so the activations
-//    are re-paired (x0, x4), (x1, x5), ... once per lane and reused over
-//    every row the lane visits.
-//
-// Work split: a lane owns 32 consecutive input elements (16 bytes of codes)
-// of a 2048-wide chunk of k; the 4 waves of a block split the chunks of k
-// (ks_count ways) and/or the block's rows; partial sums are reduced across
-// the wave with butterflies and across waves through LDS. No atomics, so
-// results are deterministic.
+//    code word into a packed bf16 pair. Products with bf16 activations are
+//    exact in fp32.
+//  * The offset and the zero point are folded into a per-group correction:
+//    sum x (q - z) s = s * (sum x (128 + q) - (128 + z) * sum x), with the
+//    activation sum formed once per activation segment.
+//  * Nibbles 0..3 of a code word pair with nibbles 4..7, so activations are
+//    re-paired (x0, x4), (x1, x5), ... when loaded.
+// Partial sums are reduced with butterflies inside a wave and through LDS
+// across waves; there are no atomics, so results are deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,7 +29,9 @@ namespace lq {
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
 constexpr uint32_t kNib = 0x000F000Fu;
 constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1, 1)
-constexpr int kChunk = 2048;              // k per wave-wide 16-byte load
+constexpr int kChunk = 2048;              // k covered by one wave-wide 16-byte load
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // 8 consecutive bf16 activations [x0 x1][x2 x3][x4 x5][x6 x7] -> pairs in
 // the order the nibble extraction produces: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
@@ -44,136 +42,312 @@ LQ_DEVICE void pair_x(const u32x4 v, uint32_t *p) {
     p[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
 }
 
-// One code word (element i of 8 at bits 4i..4i+3) against its 4 x pairs.
-LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc) {
-    acc = dot2_bf16((w & kNib) | kMagic, xp[0], acc);
-    acc = dot2_bf16(((w >> 4) & kNib) | kMagic, xp[1], acc);
-    acc = dot2_bf16(((w >> 8) & kNib) | kMagic, xp[2], acc);
-    acc = dot2_bf16(((w >> 12) & kNib) | kMagic, xp[3], acc);
+// Code word (element i of 8 at bits 4i..4i+3) -> 4 bf16 pairs (128 + c_i,
+// 128 + c_{i+4}), i = 0..3. `magic` holds kMagic (passed in a VGPR).
+LQ_DEVICE void unpack_word(uint32_t w, uint32_t *p, uint32_t magic) {
+    p[0] = (w & kNib) | magic;
+    p[1] = ((w >> 4) & kNib) | magic;
+    p[2] = ((w >> 8) & kNib) | magic;
+    p[3] = ((w >> 12) & kNib) | magic;
+}
+
+LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) {
+    uint32_t p[4];
+    unpack_word(w, p, magic);
+    acc = dot2_bf16(p[0], xp[0], acc);
+    acc = dot2_bf16(p[1], xp[1], acc);
+    acc = dot2_bf16(p[2], xp[2], acc);
+    acc = dot2_bf16(p[3], xp[3], acc);
     return acc;
 }
 
-// B: batch; RW: rows per wave-set; U: rows in flight per step.
-template <int B, int RW, int U, bool SYM>
-__global__ __launch_bounds__(256) void gemv_w4_kernel(const uint16_t *__restrict__ x,
-                                                       const uint8_t *__restrict__ codes,
-                                                       const float *__restrict__ scales,
-                                                       const float *__restrict__ zeros, int n, int k,
-                                                       int group, int ks_count,
-                                                       float *__restrict__ y) {
-    static_assert(RW % U == 0, "rows per wave-set must be a multiple of U");
-    __shared__ float red[4][RW * B];
+// Sum RW values per lane over the 64 lanes of a wave. Halving exchanges
+// first (each step sends half of the remaining values), then plain
+// butterflies. Afterwards lane l holds the total of row (l >> (6 - log2 RW)).
+template <int RW>
+LQ_DEVICE float reduce_rows(float *v, int lane) {
+    constexpr int P = RW == 1 ? 0 : RW == 2 ? 1 : RW == 4 ? 2 : RW == 8 ? 3 : RW == 16 ? 4 : 5;
+    static_assert((1 << P) == RW, "RW must be a power of two <= 32");
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+        const int m = 32 >> s;
+        const int h = RW >> (s + 1);
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const float send = upper ? v[i] : v[i + h];
+            const float keep = upper ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, m, 64);
+        }
+    }
+#pragma unroll
+    for (int m = 32 >> P; m >= 1; m >>= 1) v[0] += __shfl_xor(v[0], m, 64);
+    return v[0];
+}
+
+// ---------------------------------------------------------------------------
+// VALU kernel, batch B <= 4.
+// Block = 4 waves. The waves split the 2048-wide chunks of k (ks_count ways)
+// and the block's rows (4 / ks_count row sets of RW rows). For each chunk a
+// wave first loads and pairs its 32 activations per batch row (L2 hits),
+// then issues the 16-byte code loads (and scales, zeros) of all RW rows
+// through buffer resources that cover only its rows, so rows past n and
+// lanes past k read zeros instead of needing branches; then it computes as
+// rows arrive. Per-row partial sums stay in registers until one transposed
+// reduction at the end.
+// ---------------------------------------------------------------------------
+template <int B, int RW, bool SYM>
+__global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restrict__ x,
+                                                         const uint8_t *__restrict__ codes,
+                                                         const float *__restrict__ scales,
+                                                         const float *__restrict__ zeros, int n, int k,
+                                                         int group, int ks_count, float *__restrict__ y) {
+    __shared__ float red[4][B][RW];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform (scalar) so the buffer resources below live in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % ks_count;
     const int rs = wave / ks_count;
-    const int rsets = 4 / ks_count;
-    const int row0 = blockIdx.x * (rsets * RW) + rs * RW;
+    const int row0 = (blockIdx.x * (4 / ks_count) + rs) * RW;
     const int ng = k / group;
     const int nchunks = (k + kChunk - 1) / kChunk;
-    const int64_t row_bytes = k / 2;
+    const uint32_t row_bytes = (uint32_t)k / 2;
+    const int rows_here = row0 < n ? min(RW, n - row0) : 0;
+    const auto rc = make_rsrc(codes + (int64_t)row0 * row_bytes, rows_here * row_bytes);
+    const auto rsc = make_rsrc(scales + (int64_t)row0 * ng, rows_here * ng * 4);
+    const auto rz = make_rsrc(SYM ? scales : zeros + (int64_t)row0 * ng, SYM ? 0 : rows_here * ng * 4);
+    // 0x43004300 in a VGPR so the nibble extraction selects v_and_or_b32
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
 
-    float res[RW][B];
+    float acc[B][RW];
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int b = 0; b < B; ++b) res[r][b] = 0.0f;
+        for (int r = 0; r < RW; ++r) acc[b][r] = 0.0f;
 
     for (int c = ks; c < nchunks; c += ks_count) {
         const int k0 = c * kChunk + lane * 32;
         const bool kv = k0 < k;
+        // All loads of the chunk first: activations (L2 hits), then codes,
+        // scales and zeros of every row; nothing waits until all are issued.
+        u32x4 xv[B][4];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const auto rx = make_rsrc(x + (int64_t)b * k, (uint32_t)k * 2);
+            const uint32_t xo = kv ? (uint32_t)k0 * 2 : kOutOfRange;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * j, 0, 0);
+        }
+        const uint32_t co = kv ? (uint32_t)k0 / 2 : kOutOfRange;
+        const uint32_t so = kv ? (uint32_t)(k0 / group) * 4 : kOutOfRange;
+        u32x4 cw[RW];
+        float sc[RW], zc[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            cw[r] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + r * row_bytes, 0, kNonTemporal);
+            sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, so + r * ng * 4, 0, 0));
+            zc[r] = SYM ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, so + r * ng * 4, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t xp[B][16];
         float xs[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pair_x(xv[b][j], &xp[b][4 * j]);
             xs[b] = 0.0f;
-            if (kv) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (int64_t)b * k + k0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pair_x(src[j], &xp[b][4 * j]);
-#pragma unroll
-                for (int j = 0; j < 16; ++j) xs[b] = dot2_bf16(xp[b][j], kOnes, xs[b]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) xp[b][j] = 0u;
-            }
+            for (int j = 0; j < 16; ++j) xs[b] = dot2_bf16(xp[b][j], kOnes, xs[b]);
         }
-        const int gk = k0 / group;
 #pragma unroll
-        for (int rb = 0; rb < RW; rb += U) {
-            u32x4 cw[U];
-            float sc[U], zc[U];
+        for (int r = 0; r < RW; ++r) zc[r] = SYM ? 136.0f : 128.0f + zc[r];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = row0 + rb + u;
-                if (kv && row < n) {
-                    cw[u] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(codes + (int64_t)row * row_bytes + k0 / 2));
-                    sc[u] = scales[(int64_t)row * ng + gk];
-                    zc[u] = SYM ? 136.0f : 128.0f + zeros[(int64_t)row * ng + gk];
-                } else {
-                    cw[u] = u32x4{0u, 0u, 0u, 0u};
-                    sc[u] = 0.0f;
-                    zc[u] = 0.0f;
-                }
-            }
+        for (int r = 0; r < RW; ++r) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    float d = 0.0f;
-                    d = dot8(cw[u].x, &xp[b][0], d);
-                    d = dot8(cw[u].y, &xp[b][4], d);
-                    d = dot8(cw[u].z, &xp[b][8], d);
-                    d = dot8(cw[u].w, &xp[b][12], d);
-                    const float part = sc[u] * __builtin_fmaf(-zc[u], xs[b], d);
-                    res[rb + u][b] += team_sum<64>(part);
-                }
+            for (int b = 0; b < B; ++b) {
+                float d = 0.0f;
+                d = dot8(cw[r].x, &xp[b][0], d, magic);
+                d = dot8(cw[r].y, &xp[b][4], d, magic);
+                d = dot8(cw[r].z, &xp[b][8], d, magic);
+                d = dot8(cw[r].w, &xp[b][12], d, magic);
+                acc[b][r] = __builtin_fmaf(sc[r], __builtin_fmaf(-zc[r], xs[b], d), acc[b][r]);
             }
         }
     }
-    if (lane == 0) {
+    constexpr int P = RW == 1 ? 0 : RW == 2 ? 1 : RW == 4 ? 2 : RW == 8 ? 3 : RW == 16 ? 4 : 5;
 #pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) red[wave][r * B + b] = res[r][b];
+    for (int b = 0; b < B; ++b) {
+        const float v = reduce_rows<RW>(acc[b], lane);
+        if ((lane & ((64 >> P) - 1)) == 0) red[wave][b][lane >> (6 - P)] = v;
     }
     __syncthreads();
     if (ks == 0 && lane < RW * B) {
+        const int b = lane / RW, r = lane % RW;
         float v = 0.0f;
-        for (int w = 0; w < ks_count; ++w) v += red[rs * ks_count + w][lane];
-        const int r = lane / B, b = lane % B;
+        for (int w = 0; w < ks_count; ++w) v += red[rs * ks_count + w][b][r];
         const int row = row0 + r;
         if (row < n) y[(int64_t)b * n + row] = v;
     }
 }
 
-template <int B, bool SYM>
-static hipError_t launch_gemv_b(const W4Args &a, hipStream_t st) {
-    constexpr int RW = B == 1 ? 8 : (B <= 4 ? 4 : (B <= 8 ? 2 : 1));
-    constexpr int U = RW < 4 ? RW : 4;
+// ---------------------------------------------------------------------------
+// MFMA kernel, batch 5..16 (v_mfma_f32_16x16x32_bf16).
+// A = weights (16 rows x 32 k), B = activations (32 k x 16 batch columns,
+// zero beyond the batch), D = 16 rows x 16 columns in fp32. Lane l serves
+// weight row l % 16 and k quarter l / 16: its 16-byte code load covers 32
+// consecutive k, and MFMA step j (0..3) takes code word j, so the four steps
+// of one load cover exactly one 128-wide group. The activation operand uses
+// the same (lane, step) -> k map, re-paired to match the nibble pairs. The
+// four steps accumulate into a fresh tile per group, which is then scaled:
+// acc += s (D_g - (128 + z) X_g), X_g the group's activation sums.
+// Block = 4 waves over RT row tiles of 16 rows; the waves split the groups
+// of k and reduce through LDS.
+// ---------------------------------------------------------------------------
+template <int RT, bool SYM>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t *__restrict__ x, int bsz,
+                                                         const uint8_t *__restrict__ codes,
+                                                         const float *__restrict__ scales,
+                                                         const float *__restrict__ zeros, int n, int k,
+                                                         int group, float *__restrict__ y) {
+    __shared__ float red[4][RT][16][17];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lr = lane & 15;   // weight row within a tile (A operand) / batch column (B operand)
+    const int kq = lane >> 4;   // k quarter of the group
+    const int row_base = blockIdx.x * (16 * RT);
+    const int ng128 = k / 128;  // 128-wide sub-groups (a group is a multiple of 128)
+    const int ng = k / group;
+    const int64_t row_bytes = k / 2;
+    const bool bvalid = lr < bsz;
+    const uint16_t *xrow = x + (int64_t)(bvalid ? lr : 0) * k;
+
+    f32x4 acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int g = wave; g < ng128; g += 4) {
+        const int kb = g * 128 + kq * 32;  // this lane's 32 k of the group
+        u32x4 cw[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int row = row_base + t * 16 + lr < n ? row_base + t * 16 + lr : n - 1;
+            cw[t] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(codes + (int64_t)row * row_bytes + kb / 2));
+        }
+        // scale / zero of the 4 rows whose outputs this lane holds
+        const int gi = (g * 128) / group;
+        float sc[RT][4], zc[RT][4];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r0 = row_base + t * 16 + kq * 4 + i;
+                const int row = r0 < n ? r0 : n - 1;
+                sc[t][i] = scales[(int64_t)row * ng + gi];
+                zc[t][i] = SYM ? 0.0f : zeros[(int64_t)row * ng + gi];
+            }
+        // activations: 32 k of batch column lr, paired like the nibbles
+        uint32_t xp[16];
+        {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow + kb);
+            u32x4 xv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[j] = src[j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pair_x(xv[j], &xp[4 * j]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) xp[j] = bvalid ? xp[j] : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[t][i] = row_base + t * 16 + kq * 4 + i < n ? sc[t][i] : 0.0f;
+                zc[t][i] = SYM ? 136.0f : 128.0f + zc[t][i];
+            }
+        // X_g for column lr: sum over the 4 lanes (k quarters) of that column
+        float xs = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xs = dot2_bf16(xp[j], kOnes, xs);
+        xs += __shfl_xor(xs, 16, 64);
+        xs += __shfl_xor(xs, 32, 64);
+        bf16x8_t bop[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 v = u32x4{xp[4 * j], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]};
+            bop[j] = __builtin_bit_cast(bf16x8_t, v);
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint32_t words[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t p[4];
+                unpack_word(words[j], p, kMagic);
+                const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, u32x4{p[0], p[1], p[2], p[3]});
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[j], d, 0, 0, 0);
+            }
+            // lane holds D[row = 4 kq + i][col = lr]; the column's X_g is xs
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = __builtin_fmaf(sc[t][i], __builtin_fmaf(-zc[t][i], xs, d[i]), acc[t][i]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][t][kq * 4 + i][lr] = acc[t][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < RT * 256; e += 256) {
+        const int t = e >> 8, rr = (e >> 4) & 15, col = e & 15;
+        const float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
+        const int row = row_base + t * 16 + rr;
+        if (row < n && col < bsz) y[(int64_t)col * n + row] = v;
+    }
+}
+
+template <int B, int RW, bool SYM>
+static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
-    const int ks_count = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
+    int ks_count = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
     const int rows_per_block = (4 / ks_count) * RW;
     const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_w4_kernel<B, RW, U, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x,
-                       a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x, a.codes,
+                       a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+    return hipGetLastError();
+}
+
+// Rows per wave: 8 for tall matrices (fewer activation re-reads), 4 for short
+// ones (more blocks to fill the chip).
+template <int B, bool SYM>
+static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
+    return a.n >= 8192 ? launch_valu_rw<B, 8, SYM>(a, st) : launch_valu_rw<B, 4, SYM>(a, st);
+}
+
+template <bool SYM>
+static hipError_t launch_mfma(const W4Args &a, hipStream_t st) {
+    constexpr int RT = 2;
+    const int64_t blocks = (a.n + 16 * RT - 1) / (16 * RT);
+    hipLaunchKernelGGL((gemv_mfma_kernel<RT, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x, (int)a.m,
+                       a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, a.y);
     return hipGetLastError();
 }
 
 template <bool SYM>
 static hipError_t launch_gemv_s(const W4Args &a, hipStream_t st) {
     switch (a.m) {
-#define LQ_B(BB) \
-    case BB: return launch_gemv_b<BB, SYM>(a, st);
-        LQ_B(1) LQ_B(2) LQ_B(3) LQ_B(4) LQ_B(5) LQ_B(6) LQ_B(7) LQ_B(8)
-        LQ_B(9) LQ_B(10) LQ_B(11) LQ_B(12) LQ_B(13) LQ_B(14) LQ_B(15) LQ_B(16)
-#undef LQ_B
-        default: return hipErrorInvalidValue;
+        case 1: return launch_valu<1, SYM>(a, st);
+        case 2: return launch_valu<2, SYM>(a, st);
+        case 3: return launch_valu<3, SYM>(a, st);
+        case 4: return launch_valu<4, SYM>(a, st);
+        default: return launch_mfma<SYM>(a, st);
     }
 }
 
 hipError_t launch_w4a16_gemv(const W4Args &a, hipStream_t st) {
+    if (a.m < 1 || a.m > 16) return hipErrorInvalidValue;
     return a.symmetric ? launch_gemv_s<true>(a, st) : launch_gemv_s<false>(a, st);
 }
 

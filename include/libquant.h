@@ -136,7 +136,7 @@ lq_status dequantize_groupwise(const void *codes, const float *scales, const flo
  * codes   [n][k/2] INT4 codes from quantize_groupwise(bits = 4).
  * scales  fp32 [n][k/group]; zeros fp32 [n][k/group] or NULL if symmetric.
  * y       out fp32 [b][n].
- * group: multiple of 128 dividing k; k multiple of 128.
+ * group: multiple of 128 dividing k; k multiple of 128 and at most 2^28.
  */
 lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales,
                      const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,
