@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode token of the workload: the batch-1 W4A16 GEMV over
+every linear of every layer (for the Llama-2-70B-shaped default, 80 layers
+of q|k|v, o, gate|up and down: each fused pair or triple is one matrix whose
+rows are the concatenated rows of its parts, which per-row group
+quantization leaves unchanged), all weights resident in HBM in
+address-distinct buffers, replayed from a captured HIP graph. Headline:
+algorithmic bytes per token (codes + fp32 scales/zeros + activations +
+outputs) divided by the measured time per token.
+
+The same run also measures, live, every other step of the path on its own
+workload: group-wise quantize-pack (while building the weights), dequantize,
+the prefill W4A16 GEMM, and the SmoothQuant W8A8 steps. They are reported
+in "rows". The dominant kernel's roofline uses HIP events around each of
+its launches on the launch stream; "traffic" comes from the committed
+rocprofv3 counter summary when the kernel source still matches it. The CPU
+oracle is timed on a bounded sample and reported as "cpu_baseline".
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, published
+DOMINANT_SRC = os.path.join(ROOT, "bit_gemv_amd", "csrc", "gemv.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "gemv_w4a16_llama70b_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(path: str = DOMINANT_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def w4_bytes(n: int, k: int, b: int, symmetric: bool, group: int) -> int:
+    """Algorithmic bytes of one W4A16 product: codes, fp32 scales (+ zeros),
+    bf16 activations read, fp32 outputs written."""
+    meta = n * (k // group) * 4 * (1 if symmetric else 2)
+    return n * k // 2 + meta + b * k * 2 + b * n * 4
+
+
+def _timed(fn, reps: int = 5) -> float:
+    """Average ms of fn() over reps launches, bracketed by HIP events on the
+    current stream after one untimed call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_rows(dev, packed, shapes, names, wl) -> dict:
+    """Live measurement of every other step of the path on its own workload."""
+    import numpy as np
+    import torch
+
+    import bit_gemv_amd as bg
+    from workloads import WORKLOADS
+
+    def dev_bf16(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    rows = {}
+    # a5: dequantize (fp32 out) of one matrix per layer, across distinct layers
+    j = names.index("o") if "o" in names else 0
+    n, k = shapes[j]
+    out = torch.empty((n, k), dtype=torch.float32, device=dev)
+    it = iter(range(10 ** 9))
+    ms = _timed(lambda: bg.dequantize_groupwise(packed[next(it) % len(packed)][j], out), reps=10)
+    pw = packed[0][j]
+    byt = pw.nbytes() + n * k * 4
+    rows["dequantize"] = {"shape": [n, k], "ms": round(ms, 4), "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+                          "bound": "hbm", "frac_of_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del out
+    log(f"[bench] dequantize {n}x{k}: {rows['dequantize']['GBps']} GB/s")
+
+    # a7: prefill W4A16 GEMM, M = 2048, 70B-shaped layers
+    pf = WORKLOADS["prefill70b"]
+    gem = {}
+    for i, lin in enumerate(pf.linears):
+        w = dev_bf16(pf.weight(0, i))
+        pwq = bg.quantize_groupwise(w, 4, pf.symmetric, pf.group)
+        del w
+        x = dev_bf16(pf.activation(lin.k, pf.tokens))
+        y = torch.empty((pf.tokens, lin.n), dtype=torch.float32, device=dev)
+        try:
+            ms = _timed(lambda: bg.w4a16_gemm(x, pwq, y), reps=5)
+            tf = 2.0 * pf.tokens * lin.n * lin.k / (ms * 1e-3) / 1e12
+            gem[f"{lin.name} {lin.n}x{lin.k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                                                   "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+            log(f"[bench] w4a16_gemm M={pf.tokens} {lin.n}x{lin.k}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        except bg.LibquantError as e:
+            gem[f"{lin.name} {lin.n}x{lin.k}"] = {"error": str(e)}
+        del pwq, x, y
+    rows["w4a16_gemm_prefill"] = {"workload": pf.name, "m": pf.tokens, "bound": "mfma", "shapes": gem}
+
+    # a8-a11: SmoothQuant W8A8, X 512 x 8192 with outlier channels, W 8192 x 8192
+    sq = WORKLOADS["smoothquant"]
+    lin = sq.linears[0]
+    x = dev_bf16(sq.activation(lin.k, sq.tokens))
+    w = dev_bf16(sq.weight(0, 0))
+    t, kk, nn = sq.tokens, lin.k, lin.n
+    alpha = sq.extra["alpha"]
+    r = {}
+    s = bg.smooth_scale(x, w, alpha)
+    ms = _timed(lambda: bg.smooth_scale(x, w, alpha, s=s))
+    r["smooth_scale"] = {"ms": round(ms, 4), "GBps": round((t * kk * 2 + nn * kk * 2) / (ms * 1e-3) / 1e9, 1)}
+    pwq = bg.quantize_groupwise(w, 8, True, kk, s)
+    ms = _timed(lambda: bg.quantize_groupwise(w, 8, True, kk, s, out=pwq))
+    r["quantize_w_int8_per_channel"] = {"ms": round(ms, 4),
+                                        "GBps": round((nn * kk * 3 + nn * 4) / (ms * 1e-3) / 1e9, 1)}
+    qx, sx = bg.quant_per_token_int8(x, s)
+    ms = _timed(lambda: bg.quant_per_token_int8(x, s, qx, sx))
+    r["quant_per_token_int8"] = {"ms": round(ms, 4), "GBps": round((t * kk * 3 + t * 4) / (ms * 1e-3) / 1e9, 1)}
+    try:
+        y, acc = bg.w8a8_gemm(qx, sx, pwq.codes.view(torch.int8), pwq.scales.view(-1), want_acc=True)
+        ms = _timed(lambda: bg.w8a8_gemm(qx, sx, pwq.codes.view(torch.int8), pwq.scales.view(-1), y=y, acc=acc))
+        tops = 2.0 * t * nn * kk / (ms * 1e-3) / 1e12
+        r["w8a8_gemm"] = {"ms": round(ms, 4), "TOPs": round(tops, 1), "bound": "mfma",
+                          "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    except bg.LibquantError as e:
+        r["w8a8_gemm"] = {"error": str(e)}
+    rows["smoothquant_w8a8"] = {"workload": sq.name, "t": t, "n": nn, "k": kk, **r}
+    log(f"[bench] smoothquant rows: {r}")
+    return rows
+
+
+def cpu_baseline(wl, B, min_seconds: float = 10.0) -> dict:
+    """The CPU oracle timed on a bounded sample of the same workload: whole
+    linears of the layer stack, in order (layer 0 first), each quantized and
+    then multiplied with a batch-B activation, single thread, until about
+    min_seconds of oracle time have been spent."""
+    import oracle
+    sample_bytes = 0
+    t_q = t_mv = 0.0
+    q_bytes = 0
+    done = 0
+    while t_q + t_mv < min_seconds and done < 3 * len(wl.linears):
+        i = done % len(wl.linears)
+        lin = wl.linears[i]
+        w = wl.weight(done // len(wl.linears), i)
+        x = wl.activation(lin.k, B)
+        t0 = time.perf_counter()
+        codes, sc, zs = oracle.quantize(w, 4, wl.symmetric, wl.group)
+        t1 = time.perf_counter()
+        oracle.w4a16_matmul(x, codes, sc, zs, lin.n, lin.k, wl.symmetric, wl.group)
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        t_mv += t2 - t1
+        q_bytes += w.size * 2 + codes.nbytes + sc.nbytes + (0 if zs is None else zs.nbytes)
+        sample_bytes += w4_bytes(lin.n, lin.k, B, wl.symmetric, wl.group)
+        done += 1
+        del w, codes, sc, zs
+    log(f"[bench] cpu oracle: gemv {sample_bytes / t_mv / 1e9:.3f} GB/s, quantize {q_bytes / t_q / 1e9:.3f} GB/s")
+    return {"value": round(sample_bytes / t_mv / 1e12, 6), "unit": "TB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} linears of {wl.name} (unfused, layer-major), batch {B}: "
+                      f"{sample_bytes / 1e9:.3f} GB of GEMV in {t_mv:.1f} s",
+            "quantize_pack_GBps": round(q_bytes / t_q / 1e9, 3),
+            "quantize_sample": f"same linears, {q_bytes / 1e9:.2f} GB in {t_q:.1f} s"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama70b_decode", choices=["llama70b_decode", "llama7b_decode"])
+    ap.add_argument("--batch", type=int, default=1, help="decode batch (llama7b_decode also runs 4 and 16)")
+    ap.add_argument("--unfused", action="store_true", help="one GEMV per linear instead of fused q|k|v, gate|up")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--skip-rows", action="store_true", help="only the decode sweep")
+    ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_gemv_amd as bg
+    from workloads import WORKLOADS
+
+    bg.load_library()  # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    B = args.batch
+    sym, group = wl.symmetric, wl.group
+
+    def dev_bf16(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- weights: distinct content sets, address-distinct layers
+    if args.unfused:
+        groups = [[i] for i in range(len(wl.linears))]
+    elif args.workload == "llama70b_decode" or args.workload == "llama7b_decode":
+        groups = [[0, 1, 2], [3], [4, 5], [6]]
+    names = ["|".join(wl.linears[i].name for i in g) for g in groups]
+    shapes = [(sum(wl.linears[i].n for i in g), wl.linears[g[0]].k) for g in groups]
+    log(f"[bench] workload {wl.name}: {wl.layers} layers, matrices {list(zip(names, shapes))}, batch {B}")
+
+    t0 = time.time()
+    n_sets = min(wl.distinct_layers, 2)
+    src = []  # per content set: list of bf16 device tensors, one per fused matrix
+    for s in range(n_sets):
+        mats = []
+        for g in groups:
+            parts = [dev_bf16(wl.weight(s, i)) for i in g]
+            mats.append(torch.cat(parts, 0) if len(parts) > 1 else parts[0])
+            del parts
+        src.append(mats)
+    log(f"[bench] generated {n_sets} weight set(s) in {time.time() - t0:.1f}s")
+
+    # quantize-pack every layer into its own buffers; time it (rows: quantize_pack)
+    packed = []
+    qev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    qev[0].record()
+    for layer in range(wl.layers):
+        mats = src[layer % n_sets]
+        packed.append([bg.quantize_groupwise(m, 4, sym, group) for m in mats])
+    qev[1].record()
+    torch.cuda.synchronize()
+    q_ms = qev[0].elapsed_time(qev[1])
+    q_elems = sum(n * k for n, k in shapes) * wl.layers
+    q_bytes = q_elems * 2 + sum(p.nbytes() for lay in packed for p in lay)
+    quant_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    log(f"[bench] quantize-pack {q_elems / 1e9:.1f} G weights in {q_ms:.1f} ms: {quant_gbs:.0f} GB/s")
+    del src
+    torch.cuda.empty_cache()
+
+    # activations (one per input width) and outputs (one per matrix shape)
+    xs = {k: dev_bf16(wl.activation(k, B)) for k in sorted({k for _, k in shapes})}
+    ys = [torch.empty((B, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+
+    def sweep():
+        for layer in range(wl.layers):
+            for j, (n, k) in enumerate(shapes):
+                bg.w4a16_gemv(xs[k], packed[layer][j], ys[j])
+
+    token_bytes = wl.layers * sum(w4_bytes(n, k, B, sym, group) for n, k in shapes)
+    launches = wl.layers * len(shapes)
+
+    # ---------------- timed decode steps
+    if args.no_graph:
+        run = sweep
+    else:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sweep()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sweep()
+        run = graph.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    value_tbs = token_bytes / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {args.steps} tokens: {ms_per_step:.3f} ms/token, {token_bytes / 1e9:.2f} GB/token, "
+        f"{value_tbs:.3f} TB/s, {1e3 / ms_per_step:.1f} tokens/s")
+
+    # ---------------- dominant kernel: per-launch HIP events on the launch stream
+    dom = max(range(len(shapes)), key=lambda j: shapes[j][0] * shapes[j][1])
+    dn, dk = shapes[dom]
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)  # hold the stream so all launches queue before the GPU reaches them
+    for layer in range(wl.layers):
+        ev0[layer].record()
+        bg.w4a16_gemv(xs[dk], packed[layer][dom], ys[dom])
+        ev1[layer].record()
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    dom_us = 1e3 * sum(durs) / len(durs)
+    dom_bytes = w4_bytes(dn, dk, B, sym, group)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    log(f"[bench] dominant kernel {names[dom]} {dn}x{dk}: {dom_us:.2f} us/launch, {achieved:.0f} GB/s")
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            cnt = json.load(f)
+        if cnt.get("kernel_source_sha256_16") == kernel_source_hash() and cnt.get("n") == dn and cnt.get("k") == dk:
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": "W4A16 batch-1 GEMV effective HBM TB/s (% of peak); quantize-pack GB/s",
+        "value": round(value_tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0, 0.02^2) weights, N(0,1) activations)",
+        "config": {
+            "workload": wl.name,
+            "layers": wl.layers,
+            "batch": B,
+            "matrices": {nm: [n, k] for nm, (n, k) in zip(names, shapes)},
+            "quant": f"INT4 {'sym' if sym else 'asym'} G={group}, fp32 scale{'' if sym else '+zero'}",
+            "launches_per_token": launches,
+            "bytes_per_token": token_bytes,
+            "graph": not args.no_graph,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value_tbs * 1e3 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(1e3 / ms_per_step, 2),
+        "quantize_pack_GBps": round(quant_gbs, 1),
+        "roofline": {
+            "kernel": f"w4a16_gemv {names[dom]} {dn}x{dk} batch {B}",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
+        },
+    }
+
+    if not args.skip_rows:
+        result["rows"] = {"quantize_pack": {"workload": wl.name, "weights": q_elems, "ms": round(q_ms, 3),
+                                            "GBps": round(quant_gbs, 1), "bound": "hbm",
+                                            "frac_of_peak": round(quant_gbs / HBM_PEAK_GBS, 4)}}
+        result["rows"].update(measure_rows(dev, packed, shapes, names, wl))
+
+    del packed
+    torch.cuda.empty_cache()
+
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, B)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,6 +16,8 @@ Recipe (every tensor):
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -44,18 +46,20 @@ def outlier_channels(workload: int, k: int, count: int, layer: int = 0, matrix: 
 
 
 def normal_bf16(seed: tuple, rows: int, cols: int, sigma: float = 1.0, col_mult=None,
-                row_start: int = 0, row_stop: int | None = None) -> np.ndarray:
+                row_start: int = 0, row_stop: int | None = None, threads: int | None = None) -> np.ndarray:
     """Rows [row_start, row_stop) of a seeded rows x cols N(0, sigma^2) bf16 matrix.
 
     ``col_mult`` (optional, float32 [cols]) multiplies each column after
-    drawing. Any row range gives the same values as the full draw.
+    drawing. Any row range gives the same values as the full draw; chunks are
+    drawn on ``threads`` worker threads (default: up to 16).
     """
     if row_stop is None:
         row_stop = rows
     out = np.empty((row_stop - row_start, cols), np.uint16)
     c0 = row_start // CHUNK_ROWS
     c1 = (row_stop + CHUNK_ROWS - 1) // CHUNK_ROWS
-    for c in range(c0, c1):
+
+    def one(c):
         r0, r1 = c * CHUNK_ROWS, min(rows, (c + 1) * CHUNK_ROWS)
         rng = np.random.default_rng(np.random.SeedSequence([*seed, c]))
         blk = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
@@ -64,6 +68,14 @@ def normal_bf16(seed: tuple, rows: int, cols: int, sigma: float = 1.0, col_mult=
             blk *= col_mult[None, :]
         lo, hi = max(r0, row_start), min(r1, row_stop)
         out[lo - row_start:hi - row_start] = f32_to_bf16_bits(blk[lo - r0:hi - r0])
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    if c1 - c0 <= 1 or nthreads <= 1:
+        for c in range(c0, c1):
+            one(c)
+    else:
+        with _cf.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(one, range(c0, c1)))
     return out
 
 
