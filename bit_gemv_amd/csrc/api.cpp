@@ -251,7 +251,7 @@ lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *
     const char *fn = "w8a8_gemm";
     if (m < 0 || n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size or k <= 0", fn);
     if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
-    if (k > 133120) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 133120 could overflow the int32 accumulator", fn);
+    if (k > 131072) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 131072 could overflow the int32 accumulator", fn);
     if (m > kMaxDim || n > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
     if (m == 0 || n == 0) return LQ_OK;
     if (!qx || !aligned(qx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: qx null or not 16-byte aligned", fn);

@@ -113,7 +113,7 @@ def test_smoothquant_entry_points_reject(lib):
     assert lib.smooth_scale(A16, 8, B16, 8, 256, ctypes.c_float(1.5), C16, None) == 1
     assert lib.smooth_scale(A16, 8, B16, 8, 200, ctypes.c_float(0.5), C16, None) == 2
     assert lib.quant_per_token_int8(A16, 4, 256, P((7 << 20) + 8), B16, C16, None) == 1
-    assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 256 * 1024, None, P(9 << 20), None) == 2
+    assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 131072 + 128, None, P(9 << 20), None) == 2
     assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 256, P(9 << 20), P(9 << 20), None) == 1
 
 
