@@ -182,6 +182,97 @@ def cpu_baseline(wl, B, min_seconds: float = 10.0) -> dict:
             "quantize_sample": f"same linears, {q_bytes / 1e9:.2f} GB in {t_q:.1f} s"}
 
 
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o kt -- "
+             "python3 bench.py --steps 5 --warmup 2 --skip-cpu")
+PMC_CMD = "rocprofv3 --pmc {c} -d gpurun_out/prof_{d} -o {d} -- python3 bench.py --counter-pass"
+
+
+def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
+    """Write profiles/*.md and the counter JSON from three rocprofv3 databases."""
+    import sqlite3
+
+    from workloads import WORKLOADS
+    wl = WORKLOADS["llama70b_decode"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+
+    # kernel trace: per-kernel statistics of the library's kernels (and the rest)
+    c = sqlite3.connect(trace_db)
+    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration), grid_x "
+                     "from kernels group by name, grid_x order by sum(duration) desc").fetchall()
+    lines = ["# Kernel trace: Llama-70B-shaped decode benchmark (bench.py default run, 5 steps)", "",
+             f"Command (from the repository root on the GPU box): `cd /tmp && {TRACE_CMD}`", "",
+             "Durations from rocprofv3 --kernel-trace, microseconds. `grid` is the number of work-items.", "",
+             "| kernel | grid | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
+    dom_avg = None
+    for name, cnt, avg, mn, mx, tot, gx in rows:
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        if len(short) > 70:
+            short = short[:67] + "..."
+        lines.append(f"| `{short}` | {gx} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e6:.3f} |")
+    # the fused gate|up launch: 57344 rows / 8 rows per block -> 7168 blocks x 256 work-items
+    for name, cnt, avg, mn, mx, tot, gx in rows:
+        if "gemv_valu_kernel<1, 8, false>" in name and gx == 7168 * 256:
+            dom_avg = avg / 1e3
+    lines += ["", f"Fused gate|up batch-1 GEMV (57344 x 8192, grid {7168 * 256}): average "
+                  f"{dom_avg:.2f} us per launch." if dom_avg else ""]
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_llama70b_decode.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # counters: calibrate FETCH_SIZE / WRITE_SIZE (KiB) on the 1 GiB copy
+    def counter(db, cname):
+        cc = sqlite3.connect(db)
+        recs = cc.execute("select kernel_name, grid_size, value from counters_collection where counter_name = ? "
+                          "order by dispatch_id", (cname,)).fetchall()
+        # the three 1 GiB copies: the largest copyBuffer dispatches
+        copy = sorted((v for nm, g, v in recs if "copyBuffer" in nm), reverse=True)[:3]
+        gemv = [v for nm, g, v in recs if "gemv_valu_kernel" in nm]
+        return copy, gemv
+
+    fcopy, fgemv = counter(fetch_db, "FETCH_SIZE")
+    wcopy, wgemv = counter(write_db, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    ffac = (sum(fcopy) / len(fcopy)) / gib_kib
+    wfac = (sum(wcopy) / len(wcopy)) / gib_kib
+    f_kib = sum(fgemv) / len(fgemv)
+    w_kib = sum(wgemv) / len(wgemv)
+    n, k = 57344, 8192
+    alg = w4_bytes(n, k, 1, wl.symmetric, wl.group)
+    hbm = f_kib * 1024 / ffac + w_kib * 1024 / wfac
+    out = {"kernel": "lq::gemv_valu_kernel<1, 8, false> (w4a16_gemv, batch 1, asymmetric)",
+           "workload": "llama70b_decode fused gate|up", "n": n, "k": k,
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                                "fetch_kib": round(sum(fcopy) / len(fcopy), 1),
+                                "write_kib": round(sum(wcopy) / len(wcopy), 1),
+                                "fetch_factor": round(ffac, 5), "write_factor": round(wfac, 5)},
+           "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": round(hbm / alg, 4),
+           "commands": [f"cd /tmp && {PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
+                        f"cd /tmp && {PMC_CMD.format(c='WRITE_SIZE', d='write')}"]}
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    md = ["# HBM traffic of the batch-1 W4A16 GEMV (fused gate|up, 57344 x 8192)", "",
+          "Commands (from the repository root on the GPU box):", "",
+          *[f"- `{cmd}`" for cmd in out["commands"]], "",
+          "Each pass runs torch's copy of 1 GiB three times (calibration) and the GEMV once on each of 8 "
+          "address-distinct weight buffers. Counters are per dispatch, in KiB.", "",
+          "| quantity | value |", "|---|---|",
+          f"| copy: FETCH_SIZE for 1 GiB read | {out['copy_calibration']['fetch_kib']} KiB (factor {ffac:.4f}) |",
+          f"| copy: WRITE_SIZE for 1 GiB written | {out['copy_calibration']['write_kib']} KiB (factor {wfac:.4f}) |",
+          f"| GEMV FETCH_SIZE | {out['fetch_kib_per_dispatch']} KiB |",
+          f"| GEMV WRITE_SIZE | {out['write_kib_per_dispatch']} KiB |",
+          f"| GEMV HBM bytes (calibrated) | {out['hbm_bytes_per_launch']} |",
+          f"| GEMV algorithmic bytes | {alg} |",
+          f"| traffic / algorithmic | {out['traffic_over_algorithmic']} |", "",
+          f"Kernel source hash (gemv.hip, sha256, 16 hex): `{out['kernel_source_sha256_16']}`."]
+    with open(os.path.join(ROOT, "profiles", "gemv_w4a16_llama70b_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out))
+    return 0
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,11 +284,51 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--skip-rows", action="store_true", help="only the decode sweep")
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
+                    help="turn rocprofv3 databases (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass) into "
+                         "the summaries under profiles/ and exit")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 1 GiB copy (counter calibration), then the "
+                         "dominant GEMV once on each of 8 address-distinct layers")
     return ap.parse_args()
+
+
+def counter_pass() -> int:
+    """Kernels for the HBM-traffic counters: torch's copy of a known size (the
+    calibration), then the fused gate|up batch-1 GEMV of the Llama-70B-shaped
+    workload on 8 distinct weight buffers (more than the 256 MB cache)."""
+    import numpy as np
+    import torch
+
+    import bit_gemv_amd as bg
+    from workloads import WORKLOADS
+    bg.load_library()
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS["llama70b_decode"]
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    w = torch.cat([torch.from_numpy(wl.weight(0, i).view(np.int16)).view(torch.bfloat16).to(dev) for i in (4, 5)], 0)
+    packs = [bg.quantize_groupwise(w, 4, wl.symmetric, wl.group) for _ in range(8)]
+    del w
+    x = torch.from_numpy(wl.activation(8192, 1).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((1, packs[0].n), dtype=torch.float32, device=dev)
+    for p in packs:
+        bg.w4a16_gemv(x, p, y)
+    torch.cuda.synchronize()
+    log(f"[bench] counter pass done: copy 1 GiB x3, gemv {packs[0].n}x{packs[0].k} x{len(packs)}")
+    return 0
 
 
 def main() -> int:
     args = parse()
+    if args.counter_pass:
+        return counter_pass()
+    if args.summarize_profiles:
+        return summarize_profiles(*args.summarize_profiles)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "run with --gpus 1.", file=sys.stderr)
@@ -296,23 +427,38 @@ def main() -> int:
     log(f"[bench] {args.steps} tokens: {ms_per_step:.3f} ms/token, {token_bytes / 1e9:.2f} GB/token, "
         f"{value_tbs:.3f} TB/s, {1e3 / ms_per_step:.1f} tokens/s")
 
-    # ---------------- dominant kernel: per-launch HIP events on the launch stream
+    # ---------------- dominant kernel: HIP events on its launch stream around
+    # graph replays of 80 back-to-back launches (one per layer, distinct
+    # buffers); average per launch includes the ~1.5 us launch gaps.
     dom = max(range(len(shapes)), key=lambda j: shapes[j][0] * shapes[j][1])
     dn, dk = shapes[dom]
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+
+    def dom_sweep():
+        for layer in range(wl.layers):
+            bg.w4a16_gemv(xs[dk], packed[layer][dom], ys[dom])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dom_sweep()
+    torch.cuda.current_stream().wait_stream(side)
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        dom_sweep()
+    dgraph.replay()
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)  # hold the stream so all launches queue before the GPU reaches them
-    for layer in range(wl.layers):
-        ev0[layer].record()
-        bg.w4a16_gemv(xs[dk], packed[layer][dom], ys[dom])
-        ev1[layer].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.steps // 2)
+    e0.record()
+    for _ in range(reps):
+        dgraph.replay()
+    e1.record()
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
-    dom_us = 1e3 * sum(durs) / len(durs)
+    dom_us = 1e3 * e0.elapsed_time(e1) / (reps * wl.layers)
     dom_bytes = w4_bytes(dn, dk, B, sym, group)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     log(f"[bench] dominant kernel {names[dom]} {dn}x{dk}: {dom_us:.2f} us/launch, {achieved:.0f} GB/s")
+    del dgraph
 
     traffic = None
     if os.path.exists(COUNTERS):
