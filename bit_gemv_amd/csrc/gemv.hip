@@ -96,13 +96,22 @@ LQ_DEVICE float reduce_rows(float *v, int lane) {
 // rows arrive. Per-row partial sums stay in registers until one transposed
 // reduction at the end.
 // ---------------------------------------------------------------------------
-template <int B, int RW, bool SYM>
+// G128: group == 128 and k a multiple of 512. Then all scales (and zeros) a wave needs for one chunk
+// -- RW rows x 16 groups -- come from a single 16-byte load per lane (lanes
+// 0..4RW-1 scales, the next 4RW lanes zeros), are transposed through the
+// wave's own LDS slice and read back four rows per ds_read_b128. Per-row
+// 4-byte loads would otherwise be 2 RW of the wave's vector-memory
+// instructions per chunk, and instruction issue, not bytes, bounds the
+// kernel at that point.
+template <int B, int RW, bool SYM, bool G128>
 __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restrict__ x,
                                                          const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ scales,
                                                          const float *__restrict__ zeros, int n, int k,
                                                          int group, int ks_count, float *__restrict__ y) {
+    static_assert(!G128 || RW == 4 || RW == 8, "scale staging assumes 4 or 8 rows per wave");
     __shared__ float red[4][B][RW];
+    __shared__ __attribute__((aligned(16))) float sz_lds[G128 ? 4 : 1][2][16][RW];
     const int lane = threadIdx.x & 63;
     // wave-uniform (scalar) so the buffer resources below live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -140,16 +149,63 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restri
             for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * j, 0, 0);
         }
         const uint32_t co = kv ? (uint32_t)k0 / 2 : kOutOfRange;
-        const uint32_t so = kv ? (uint32_t)(k0 / group) * 4 : kOutOfRange;
         u32x4 cw[RW];
         float sc[RW], zc[RW];
+        u32x4 szv;  // G128: this lane's four scales or zeros of one row
+        if (G128) {
+            // lane L < 4 RW: scales of row L / 4, groups 4 (L % 4) .. + 3 of the
+            // chunk; lanes 4 RW .. 8 RW - 1: the same for zeros
+            const int which = lane / (4 * RW), lr = lane % (4 * RW);
+            const int g0 = c * (kChunk / 128) + 4 * (lr & 3);
+            const uint32_t off = g0 < ng ? (uint32_t)((lr >> 2) * ng + g0) * 4 : kOutOfRange;
+            // two loads with wave-uniform descriptors; the other lanes read zeros
+            const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rsc, which == 0 ? off : kOutOfRange, 0, 0);
+            const u32x4 zv = SYM ? u32x4{0u, 0u, 0u, 0u}
+                                 : __builtin_amdgcn_raw_buffer_load_b128(rz, which == 1 ? off : kOutOfRange, 0, 0);
+            szv = which == 0 ? sv : zv;
+        }
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
+        for (int r = 0; r < RW; ++r)
             cw[r] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + r * row_bytes, 0, kNonTemporal);
-            sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, so + r * ng * 4, 0, 0));
-            zc[r] = SYM ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, so + r * ng * 4, 0, 0));
+        if (!G128) {
+            const uint32_t so = kv ? (uint32_t)(k0 / group) * 4 : kOutOfRange;
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, so + r * ng * 4, 0, 0));
+                zc[r] = SYM ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, so + r * ng * 4, 0, 0));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (G128) {
+            // transpose through LDS: [which][group in chunk][row]
+            const int which = lane / (4 * RW), lr = lane % (4 * RW);
+            if (which < 2) {
+                // (__uint_as_float, not __builtin_bit_cast: this clang reads a
+                // bit-cast vector element from the vector's first element)
+                const int gg = 4 * (lr & 3), rr = lr >> 2;
+                sz_lds[wave][which][gg + 0][rr] = __uint_as_float(szv.x);
+                sz_lds[wave][which][gg + 1][rr] = __uint_as_float(szv.y);
+                sz_lds[wave][which][gg + 2][rr] = __uint_as_float(szv.z);
+                sz_lds[wave][which][gg + 3][rr] = __uint_as_float(szv.w);
+            }
+            // the writes above and reads below are in one wave: LDS executes a
+            // wave's operations in order; keep the compiler from reordering
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int gl = lane >> 2;            // group of this lane's 32 k within the chunk
+#pragma unroll
+            for (int r4 = 0; r4 < RW; r4 += 4) {
+                const f32x4 sv = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][0][gl][r4]);
+                sc[r4] = sv.x; sc[r4 + 1] = sv.y; sc[r4 + 2] = sv.z; sc[r4 + 3] = sv.w;
+                if (!SYM) {
+                    const f32x4 zv = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][1][gl][r4]);
+                    zc[r4] = zv.x; zc[r4 + 1] = zv.y; zc[r4 + 2] = zv.z; zc[r4 + 3] = zv.w;
+                } else {
+                    zc[r4] = zc[r4 + 1] = zc[r4 + 2] = zc[r4 + 3] = 0.0f;
+                }
+            }
+        }
         uint32_t xp[B][16];
         float xs[B];
 #pragma unroll
@@ -161,7 +217,10 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restri
             for (int j = 0; j < 16; ++j) xs[b] = dot2_bf16(xp[b][j], kOnes, xs[b]);
         }
 #pragma unroll
-        for (int r = 0; r < RW; ++r) zc[r] = SYM ? 136.0f : 128.0f + zc[r];
+        for (int r = 0; r < RW; ++r) {
+            sc[r] = kv ? sc[r] : 0.0f;
+            zc[r] = SYM ? 136.0f : 128.0f + zc[r];
+        }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
 #pragma unroll
@@ -310,12 +369,18 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t *__restri
 
 template <int B, int RW, bool SYM>
 static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st) {
+    // staged scales need whole 4-group runs per row: k a multiple of 512
+    const bool g128 = a.group == 128 && a.k % 512 == 0;
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
     int ks_count = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
     const int rows_per_block = (4 / ks_count) * RW;
     const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x, a.codes,
-                       a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+    if (g128)
+        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, true>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x,
+                           a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+    else
+        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, false>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x,
+                           a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
     return hipGetLastError();
 }
 
