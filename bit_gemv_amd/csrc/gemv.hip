@@ -61,28 +61,55 @@ LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) 
     return acc;
 }
 
-// Sum RW values per lane over the 64 lanes of a wave. Halving exchanges
-// first (each step sends half of the remaining values), then plain
-// butterflies. Afterwards lane l holds the total of row (l >> (6 - log2 RW)).
+// DPP lane moves inside rows of 16 lanes (gfx9 DPP control codes)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16 lanes
+
+template <int CTRL>
+LQ_DEVICE float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Transposed exchange across lane halves of width 32 (or 16): afterwards the
+// lanes of the lower half hold a + (partner's a), those of the upper half
+// b + (partner's b). v_permlane{32,16}_swap trades the upper half of its
+// first operand for the lower half of its second.
+LQ_DEVICE float swap_add32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+LQ_DEVICE float swap_add16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum RW (4 or 8) values per lane over the 64 lanes of a wave. Each halving
+// step sends half of the remaining values to the partner lane (lane bits 5,
+// 4, then 3), plain butterflies finish the rest. Afterwards every lane l
+// holds the total of row l >> (6 - log2 RW).
 template <int RW>
 LQ_DEVICE float reduce_rows(float *v, int lane) {
-    constexpr int P = RW == 1 ? 0 : RW == 2 ? 1 : RW == 4 ? 2 : RW == 8 ? 3 : RW == 16 ? 4 : 5;
-    static_assert((1 << P) == RW, "RW must be a power of two <= 32");
+    static_assert(RW == 4 || RW == 8, "RW must be 4 or 8");
 #pragma unroll
-    for (int s = 0; s < P; ++s) {
-        const int m = 32 >> s;
-        const int h = RW >> (s + 1);
-        const bool upper = (lane & m) != 0;
+    for (int i = 0; i < RW / 2; ++i) v[i] = swap_add32(v[i], v[i + RW / 2]);
 #pragma unroll
-        for (int i = 0; i < h; ++i) {
-            const float send = upper ? v[i] : v[i + h];
-            const float keep = upper ? v[i + h] : v[i];
-            v[i] = keep + __shfl_xor(send, m, 64);
-        }
+    for (int i = 0; i < RW / 4; ++i) v[i] = swap_add16(v[i], v[i + RW / 4]);
+    float t = v[0];
+    if (RW == 8) {
+        // partner lane l ^ 15 sits across bit 3: lanes with bit 3 clear keep row 0 of the pair
+        const bool upper = (lane & 8) != 0;
+        const float keep = upper ? v[1] : v[0];
+        const float send = upper ? v[0] : v[1];
+        t = keep + dpp_move<kDppMirror>(send);
+    } else {
+        t += dpp_move<kDppMirror>(t);
     }
-#pragma unroll
-    for (int m = 32 >> P; m >= 1; m >>= 1) v[0] += __shfl_xor(v[0], m, 64);
-    return v[0];
+    t += dpp_move<kDppHalfMirror>(t);
+    t += dpp_move<kDppXor2>(t);
+    t += dpp_move<kDppXor1>(t);
+    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -115,9 +142,11 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restri
     const int lane = threadIdx.x & 63;
     // wave-uniform (scalar) so the buffer resources below live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ks = wave % ks_count;
-    const int rs = wave / ks_count;
-    const int row0 = (blockIdx.x * (4 / ks_count) + rs) * RW;
+    // ks_count is 1, 2 or 4
+    const int ks_log = ks_count == 4 ? 2 : ks_count - 1;
+    const int ks = wave & (ks_count - 1);
+    const int rs = wave >> ks_log;
+    const int row0 = (blockIdx.x * (4 >> ks_log) + rs) * RW;
     const int ng = k / group;
     const int nchunks = (k + kChunk - 1) / kChunk;
     const uint32_t row_bytes = (uint32_t)k / 2;
@@ -234,7 +263,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restri
             }
         }
     }
-    constexpr int P = RW == 1 ? 0 : RW == 2 ? 1 : RW == 4 ? 2 : RW == 8 ? 3 : RW == 16 ? 4 : 5;
+    constexpr int P = RW == 4 ? 2 : 3;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float v = reduce_rows<RW>(acc[b], lane);
@@ -368,11 +397,9 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t *__restri
 }
 
 template <int B, int RW, bool SYM>
-static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st) {
+static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st, int ks_count) {
     // staged scales need whole 4-group runs per row: k a multiple of 512
     const bool g128 = a.group == 128 && a.k % 512 == 0;
-    const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
-    int ks_count = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
     const int rows_per_block = (4 / ks_count) * RW;
     const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
     if (g128)
@@ -384,11 +411,16 @@ static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Rows per wave: 8 for tall matrices (fewer activation re-reads), 4 for short
-// ones (more blocks to fill the chip).
+// Launch shape (measured on MI355X): long rows (8 or more chunks of k) take 8
+// rows per wave with the chunks split two ways; tall matrices 8 rows per wave
+// with a four-way split; short ones 4 rows per wave (more blocks to fill the
+// chip).
 template <int B, bool SYM>
 static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
-    return a.n >= 8192 ? launch_valu_rw<B, 8, SYM>(a, st) : launch_valu_rw<B, 4, SYM>(a, st);
+    const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
+    if (nchunks >= 8) return launch_valu_rw<B, 8, SYM>(a, st, 2);
+    const int ks = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
+    return a.n >= 16384 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
 }
 
 template <bool SYM>

@@ -33,6 +33,15 @@ def test_batch1_shapes(n, k, sym):
     _case(n, k, 1, sym)
 
 
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(16384 + 37, 2048 + 512), (20000, 8192), (32768 + 5, 4096), (16400, 512),
+                                 (1003, 16384 + 512), (3001, 28672)])
+def test_tall_batch1(n, k, sym):
+    """Tall matrices and long rows (8 rows per wave, k split 1, 2 or 4 ways
+    across the block's waves), with ragged rows and a partial last chunk."""
+    _case(n, k, 1, sym, seed=n % 97)
+
+
 @pytest.mark.parametrize("b", [2, 3, 4, 5, 7, 8, 11, 16])
 @pytest.mark.parametrize("sym", [False, True])
 def test_batches(b, sym):
