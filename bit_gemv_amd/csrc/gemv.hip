@@ -411,16 +411,16 @@ static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st, int ks_count) 
     return hipGetLastError();
 }
 
-// Launch shape (measured on MI355X): long rows (8 or more chunks of k) take 8
-// rows per wave with the chunks split two ways; tall matrices 8 rows per wave
-// with a four-way split; short ones 4 rows per wave (more blocks to fill the
-// chip).
+// Launch shape (measured on MI355X): the block's four waves split k four
+// ways when a row has 4..7 chunks, two ways when it has 2..3 or 8 and more
+// (then each wave walks several chunks), not at all for one chunk; a wave
+// takes 8 rows unless that leaves fewer than 512 blocks to fill the chip.
 template <int B, bool SYM>
 static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
-    if (nchunks >= 8) return launch_valu_rw<B, 8, SYM>(a, st, 2);
-    const int ks = nchunks >= 4 ? 4 : (nchunks >= 2 ? 2 : 1);
-    return a.n >= 16384 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
+    const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
+    const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
+    return blocks8 >= 512 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
 }
 
 template <bool SYM>

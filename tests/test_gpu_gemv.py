@@ -35,10 +35,11 @@ def test_batch1_shapes(n, k, sym):
 
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("n,k", [(16384 + 37, 2048 + 512), (20000, 8192), (32768 + 5, 4096), (16400, 512),
-                                 (1003, 16384 + 512), (3001, 28672)])
+                                 (8192 + 3, 16384 + 512), (3001, 28672), (12000 + 7, 4096 + 128)])
 def test_tall_batch1(n, k, sym):
-    """Tall matrices and long rows (8 rows per wave, k split 1, 2 or 4 ways
-    across the block's waves), with ragged rows and a partial last chunk."""
+    """Tall matrices and long rows (4 or 8 rows per wave, k split 1, 2 or 4
+    ways across the block's waves, staged and per-row scale loads), with
+    ragged rows and a partial last chunk."""
     _case(n, k, 1, sym, seed=n % 97)
 
 
