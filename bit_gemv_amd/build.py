@@ -33,12 +33,19 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-Wall", "-Wno-unused-function",
 ]
+# Per-source extras. The MFMA kernels keep their accumulators in VGPRs: with
+# the default heuristic the register allocator places loop-carried MFMA
+# accumulators in AGPRs and shuffles them with v_accvgpr moves every
+# iteration.
+EXTRA = {
+    "w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *CXXFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CXXFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

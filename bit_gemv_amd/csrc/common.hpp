@@ -52,6 +52,15 @@ LQ_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any resource used here
 constexpr int kNonTemporal = 2;                // buffer-load cache policy: streaming
 
+// Workgroup barrier ordering LDS accesses only. __syncthreads() also
+// releases global memory, which makes each wave wait for all of its
+// outstanding global loads; this one leaves prefetches in flight.
+LQ_DEVICE void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // v_dot2_f32_bf16: acc + a.lo * b.lo + a.hi * b.hi, with both pairs passed
 // as packed 32-bit words.
 LQ_DEVICE float dot2_bf16(uint32_t a, uint32_t b, float acc) {

@@ -113,8 +113,8 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const uint32_t col = wn * 64 + nt * 16 + l16;
-            cw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rc, col * row_bytes + g * (GK / 2) + kq * 16, 0,
-                                                           kNonTemporal);
+            // cached: the same code words are read by every m-block
+            cw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rc, col * row_bytes + g * (GK / 2) + kq * 16, 0, 0);
             sc[nt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (col * ng + gi) * 4, 0, 0));
             zc[nt] = SYM ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, (col * ng + gi) * 4, 0, 0));
         }

@@ -8,10 +8,19 @@
 //   acc[m][n] = sum_j qx[m][j] qw[n][j]  (exact int32)
 //   y[m][n]   = ((float) acc[m][n] * sx[m]) * sw[n]
 // Both operands are K-contiguous, so a lane's 16-byte slice of a row is an
-// MFMA operand fragment as loaded. A block of 4 waves computes 128 x 128
-// outputs (2 x 2 waves of 64 x 64 = 4 x 4 tiles of 16 x 16); per 64-wide
-// k-step it stages the 128 x 64 slices of qx and qw in LDS (double-buffered,
-// rows padded to 80 bytes so fragment reads are bank-conflict-free).
+// MFMA operand fragment. A block of 4 waves computes 128 x 128 outputs (2 x 2
+// waves of 64 x 64 = 4 x 4 tiles of 16 x 16) and walks k in 64-wide steps.
+// The step's 128 x 64 slices of qx and qw go straight from memory into LDS
+// (buffer loads with the LDS-write form, 16 bytes a lane), into a ring of
+// kStages slots filled kStages - 1 steps ahead, so one wave per SIMD keeps
+// several steps of loads in flight while its MFMAs run. No VGPRs hold
+// staged data.
+// LDS slot layout: 128 rows of 64 bytes per operand; the four 16-byte chunks
+// of row r are stored XOR-permuted by swz(r) so that the 16 rows read by one
+// fragment load hit distinct banks.
+// Blocks are mapped XCD-aware: the hardware deals block b to XCD b % 8, and
+// the blocks that share a 128-row slice of qw are put on one XCD so the
+// slice is fetched into that XCD's L2 once.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,42 +31,81 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LROW = BK + 16;  // padded LDS row, bytes
+constexpr int kStages = 6;                      // LDS ring depth
+constexpr int kSlot = (BM + BN) * BK;           // bytes of one ring slot (qx rows, then qw rows)
+constexpr int kLoadsPerStep = kSlot / 1024 / 4; // 1 KB loads per wave per step
+// vmcnt limits (literals: they are pasted into the step barrier's asm)
+#define kVmPrologue 16  // (kStages - 2) steps of loads may stay pending
+#define kVmStep 12      // (kStages - 3) steps
+
+LQ_DEVICE int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt immediate (gfx9 layout): vmcnt(0), expcnt and lgkmcnt not waited on
+constexpr int kWaitVm0 = 0x0F70;
+
+#define LQ_STR2(x) #x
+#define LQ_STR(x) LQ_STR2(x)
 
 __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx, const float *__restrict__ sx,
                                                     int m, const int8_t *__restrict__ qw,
                                                     const float *__restrict__ sw, int n, int k,
                                                     int32_t *__restrict__ accout, float *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) int8_t a_lds[2][BM * LROW];
-    __shared__ __attribute__((aligned(16))) int8_t b_lds[2][BN * LROW];
+    __shared__ __attribute__((aligned(1024))) int8_t ring[kStages][kSlot];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int l16 = lane & 15, kq = lane >> 4;
 
+    // tile of this block
+    const int nt = (n + BN - 1) / BN, mt = (m + BM - 1) / BM;
+    int tn, tm;
+    if ((nt & 7) == 0) {
+        const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+        tn = xcd * (nt >> 3) + idx / mt;
+        tm = idx % mt;
+    } else {
+        tn = blockIdx.x % nt;
+        tm = blockIdx.x / nt;
+    }
+    const int n0 = tn * BN, m0 = tm * BM;
+
+    // rows past m (n) read zeros, or leave stale bytes, in LDS; they only
+    // feed outputs that are never stored
     const int rows_m = min(BM, m - m0), rows_n = min(BN, n - n0);
     const auto ra = make_rsrc(qx + (int64_t)m0 * k, (uint32_t)rows_m * (uint32_t)k);
     const auto rb = make_rsrc(qw + (int64_t)n0 * k, (uint32_t)rows_n * (uint32_t)k);
 
-    // staging: each 128 x 64 slice is 512 chunks of 16 bytes; thread t moves
-    // chunks t and t + 256 of each operand: row t / 4 (+ 64), column 16 (t % 4)
-    const int st_row = tid >> 2, st_col = (tid & 3) * 16;
-    u32x4 sa[2], sb[2];
-    auto load_stage = [&](int ks) {
+    // This wave's loads: 1 KB pieces q = 4 wave + i (i < 4) of a slot; piece
+    // q < 8 covers qx rows 16 q .. + 15, piece q >= 8 qw rows 16 (q - 8) ...
+    // Lane l writes LDS bytes 16 l of the piece: row 16 q' + l / 4, chunk
+    // slot l % 4, which holds the row's logical chunk (l % 4) ^ swz(row).
+    uint32_t src_off[kLoadsPerStep];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t off = (uint32_t)(st_row + 64 * i) * (uint32_t)k + ks * BK + st_col;
-            sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, kNonTemporal);
-        }
-    };
-    auto store_stage = [&](int buf) {
+    for (int i = 0; i < kLoadsPerStep; ++i) {
+        const int q = 4 * wave + i;
+        const int row = 16 * (q & 7) + (lane >> 2);
+        src_off[i] = (uint32_t)row * (uint32_t)k + 16u * (uint32_t)((lane & 3) ^ swz(row));
+    }
+    const int nsteps = k / BK;
+    auto issue = [&](int ks) {
+        int8_t *slot = ring[ks % kStages];
+        const bool in = ks < nsteps;  // later steps only keep the load count uniform
+        // waves 0, 1 load qx pieces, waves 2, 3 qw pieces (wave-uniform branch);
+        // plain cached loads: every qw slice is read by all m-blocks of its
+        // XCD, so it must stay in L2
+        if (wave < 2) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4 *>(&a_lds[buf][(st_row + 64 * i) * LROW + st_col]) = sa[i];
-            *reinterpret_cast<u32x4 *>(&b_lds[buf][(st_row + 64 * i) * LROW + st_col]) = sb[i];
+            for (int i = 0; i < kLoadsPerStep; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (__attribute__((address_space(3))) void *)(slot + 1024 * (4 * wave + i)), 16,
+                    in ? src_off[i] + (uint32_t)ks * BK : kOutOfRange, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kLoadsPerStep; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (__attribute__((address_space(3))) void *)(slot + 1024 * (4 * wave + i)), 16,
+                    in ? src_off[i] + (uint32_t)ks * BK : kOutOfRange, 0, 0, 0);
         }
     };
 
@@ -67,35 +115,84 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    const int nsteps = k / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nsteps) load_stage(ks + 1);
-        // fragments: lane (row l16, k quarter kq) holds 16 consecutive bytes
-        i32x4 af[4], bf[4];
+    // fragment addresses within a slot: lane (row l16, k quarter kq)
+    int a_off[4], b_off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int ra_row = wm * 64 + t * 16 + l16, rb_row = wn * 64 + t * 16 + l16;
+        a_off[t] = ra_row * BK + 16 * (kq ^ swz(ra_row));
+        b_off[t] = BM * BK + rb_row * BK + 16 * (kq ^ swz(rb_row));
+    }
+
+    // The row and column scales of this lane's outputs, loaded up front
+    // (rows past m and columns past n read zeros): the epilogue's stores then
+    // never wait on a load. These loads precede every LDS-write load, so the
+    // step waits below still count only the latter.
+    const auto rsx = make_rsrc(sx + m0, (uint32_t)rows_m * 4);
+    const auto rsw = make_rsrc(sw + n0, (uint32_t)rows_n * 4);
+    float swc[4], sxr[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        swc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rsw, (uint32_t)(wn * 64 + j * 16 + l16) * 4, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            sxr[i][v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rsx, (uint32_t)(wm * 64 + i * 16 + kq * 4 + v) * 4, 0, 0));
+    auto read_frags = [&](int ks, i32x4 *af, i32x4 *bf) {
+        const int8_t *slot = ring[ks % kStages];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            af[t] = *reinterpret_cast<const i32x4 *>(&a_lds[buf][(wm * 64 + t * 16 + l16) * LROW + kq * 16]);
-            bf[t] = *reinterpret_cast<const i32x4 *>(&b_lds[buf][(wn * 64 + t * 16 + l16) * LROW + kq * 16]);
+            af[t] = *reinterpret_cast<const i32x4 *>(slot + a_off[t]);
+            bf[t] = *reinterpret_cast<const i32x4 *>(slot + b_off[t]);
         }
+    };
+    auto mfmas = [&](const i32x4 *af, const i32x4 *bf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        if (ks + 1 < nsteps) {
-            store_stage(buf ^ 1);
-            __syncthreads();
-        }
+    };
+    // Step barrier. LDS-write loads are counted by vmcnt only and the
+    // compiler does not track them, so the waits are explicit: a wave's own
+    // loads of a step are done once at most N later loads are pending; after
+    // the barrier every wave's are. No lgkmcnt wait: the only LDS reads of the
+    // slot a step refills fed MFMAs of the step before, so they are complete,
+    // and the next step's fragment reads stay in flight across the barrier.
+#define LQ_STEP_SYNC(N) asm volatile("s_waitcnt vmcnt(" LQ_STR(N) ")\n\ts_barrier" ::: "memory")
+
+    // Pipeline: step ks's fragments were read from LDS during step ks - 1, so
+    // step ks reads step ks + 1's while its MFMAs run; the loads run
+    // kStages - 1 steps ahead. Step ks's barrier certifies that step ks + 1
+    // has landed and that every wave has finished step ks - 1, whose slot
+    // (read during step ks - 2) the step's load then refills.
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s);
+    i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+    LQ_STEP_SYNC(kVmPrologue);
+    read_frags(0, fa0, fb0);
+    for (int ks = 0; ks < nsteps; ks += 2) {  // nsteps is even: k is a multiple of 128
+        LQ_STEP_SYNC(kVmStep);
+        issue(ks + kStages - 1);
+        read_frags(ks + 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        LQ_STEP_SYNC(kVmStep);
+        issue(ks + kStages);
+        read_frags(ks + 2, fa0, fb0);  // past the last step: read, never used
+        mfmas(fa1, fb1);
     }
+#undef LQ_STEP_SYNC
+    // drain the trailing (out-of-range) loads and the scale loads; the
+    // builtin (unlike an asm wait) tells the compiler nothing is pending, so
+    // the guarded stores below carry no further waits
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // epilogue: lane holds acc[row 4 kq + v][col l16] of each tile
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + j * 16 + l16;
-        const float swc = col < n ? sw[col] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -104,17 +201,19 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
                 if (row < m && col < n) {
                     const int32_t a = acc[i][j][v];
                     if (accout) accout[(int64_t)row * n + col] = a;
-                    y[(int64_t)row * n + col] = ((float)a * sx[row]) * swc;
+                    y[(int64_t)row * n + col] = ((float)a * sxr[i][v]) * swc[j];
                 }
             }
     }
 }
+static_assert(kLoadsPerStep * (kStages - 2) == kVmPrologue && kLoadsPerStep * (kStages - 3) == kVmStep,
+              "the vmcnt counts in the step barriers");
 
 }  // namespace
 
 hipError_t launch_w8a8_gemm(const W8Args &a, hipStream_t st) {
-    dim3 grid((uint32_t)((a.n + BN - 1) / BN), (uint32_t)((a.m + BM - 1) / BM));
-    hipLaunchKernelGGL(w8a8_kernel, grid, dim3(256), 0, st, a.qx, a.sx, (int)a.m, a.qw, a.sw, (int)a.n, (int)a.k,
+    const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
+    hipLaunchKernelGGL(w8a8_kernel, dim3(blocks), dim3(256), 0, st, a.qx, a.sx, (int)a.m, a.qw, a.sw, (int)a.n, (int)a.k,
                        a.acc, a.y);
     return hipGetLastError();
 }
