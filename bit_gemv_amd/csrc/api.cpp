@@ -200,7 +200,7 @@ lq_status w4a16_gemm(const void *x_bf16, int64_t m, const void *codes, const flo
     lq_status st = check_w4(fn, x_bf16, m, codes, scales, zeros, n, k, symmetric, group, y);
     if (st != LQ_OK || m == 0 || n == 0) return st;
     // a 128-row activation tile is addressed with 32-bit buffer offsets
-    if (k > (int64_t(1) << 24)) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 2^24", fn);
+    if (k >= (int64_t(1) << 24)) return fail(LQ_ERR_UNSUPPORTED, "%s: k >= 2^24", fn);
     if ((st = need_device()) != LQ_OK) return st;
     lq::W4Args a{static_cast<const uint16_t *>(x_bf16), m, static_cast<const uint8_t *>(codes), scales, zeros,
                  n, k, symmetric, group, y};

@@ -149,7 +149,7 @@ lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const flo
  * Runs on bf16 MFMA with exact integer weight operands and the per-group
  * scale applied in fp32.
  * x_bf16 [m][k]; y out fp32 [m][n]. Other arguments as w4a16_gemv, with
- * k at most 2^24.
+ * k below 2^24 (LQ_ERR_UNSUPPORTED otherwise).
  */
 lq_status w4a16_gemm(const void *x_bf16, int64_t m, const void *codes, const float *scales,
                      const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,

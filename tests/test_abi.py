@@ -108,6 +108,17 @@ def test_gemv_rejects(lib, args, status):
     assert lib.w4a16_gemv(*args, None) == status
 
 
+def test_gemm_rejects_k_beyond_32bit_tile_offsets(lib):
+    """A 128-row bf16 activation tile of k = 2^24 spans exactly 2^32 bytes,
+    past the kernel's 32-bit buffer offsets: refused, largest k below works
+    its way to the device check."""
+    k = 1 << 24
+    x, codes, scales, y = P(1 << 40), P(2 << 40), P(3 << 40), P(4 << 40)
+    assert lib.w4a16_gemm(x, 1, codes, scales, None, 8, k, 1, 128, y, None) == 2
+    if torch.cuda.device_count() == 0:
+        assert lib.w4a16_gemm(x, 1, codes, scales, None, 8, k - 128, 1, 128, y, None) == 4
+
+
 def test_smoothquant_entry_points_reject(lib):
     assert lib.smooth_scale(A16, 0, B16, 8, 256, ctypes.c_float(0.5), C16, None) == 1
     assert lib.smooth_scale(A16, 8, B16, 8, 256, ctypes.c_float(1.5), C16, None) == 1
