@@ -39,6 +39,7 @@ CXXFLAGS = [
 # iteration.
 EXTRA = {
     "w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -14,10 +14,18 @@
 //  * the fp32 correction acc += s (D_g - (128 + z) X_g) applies scale and
 //    zero point exactly once per group; no weight is ever rounded to bf16.
 // Tiles: a block of 4 waves computes 128 x 128 outputs (2 x 2 waves of
-// 64 x 64 = 4 x 4 MFMA tiles of 16 x 16). Per group the block stages the
-// 128 x 128 activation tile in LDS (double-buffered, padded rows); each wave
-// loads its own code words from HBM (one 16-byte load per lane per 16
-// columns) and unpacks them in registers.
+// 64 x 64 = 4 x 4 MFMA tiles of 16 x 16) and walks k one 128-wide group per
+// step. A step's 128 x 128 activation tile (32 KB) and the 128 columns' code
+// words (8 KB) go straight from memory into one slot of an LDS ring (buffer
+// loads with the LDS-write form, 16 bytes a lane), kStages - 1 steps ahead;
+// so do the 128 columns' scales and zeros of the step's group (one 4-byte
+// load form per wave: waves 0, 1 scales, waves 2, 3 zeros).
+// LDS slot layout: activation rows of 256 bytes whose sixteen 16-byte chunks
+// are XOR-permuted by (row & 15), then code columns of 64 bytes whose four
+// chunks are XOR-permuted by swz(col): the 16 rows (columns) read by one
+// fragment load hit distinct banks.
+// Blocks are mapped XCD-aware: the hardware deals block b to XCD b % 8, and
+// the blocks that share a 128-column slice of the codes are put on one XCD.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,10 +36,27 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BN = 128, GK = 128;  // block tile and group width
-constexpr int LDS_ROW = GK + 8;                // padded row (bf16): 272 bytes
+constexpr int kStages = 3;                    // LDS ring depth
+constexpr int kXBytes = BM * GK * 2;          // activation tile of a step
+constexpr int kCBytes = BN * GK / 2;          // code tile of a step
+constexpr int kSZOff = kXBytes + kCBytes;     // then 128 scales and 128 zeros (fp32)
+constexpr int kSlot = kSZOff + 2 * BN * 4;
+constexpr int kPiecesPerWave = (kXBytes + kCBytes) / 1024 / 4;  // 16-byte loads per wave per step
+constexpr int kLoadsPerWave = kPiecesPerWave + 1;               // and one 4-byte load (scales or zeros)
+// vmcnt literal pasted into the step barrier: (kStages - 2) steps of loads
+#define LQ_GEMM_VM_STEP 11
+static_assert(LQ_GEMM_VM_STEP == (kStages - 2) * kLoadsPerWave, "step barrier vmcnt");
+
 constexpr uint32_t kNibPair = 0x000F000Fu;
-constexpr uint32_t kMagicPair = 0x43004300u;   // bf16 pair (128, 128)
-constexpr uint32_t kOnePair = 0x3F803F80u;     // bf16 pair (1, 1)
+constexpr uint32_t kMagicPair = 0x43004300u;  // bf16 pair (128, 128)
+constexpr uint32_t kOnePair = 0x3F803F80u;    // bf16 pair (1, 1)
+// s_waitcnt immediate (gfx9 layout): vmcnt(0), expcnt and lgkmcnt not waited on
+constexpr int kWaitVm0 = 0x0F70;
+
+#define LQ_GEMM_STR2(x) #x
+#define LQ_GEMM_STR(x) LQ_GEMM_STR2(x)
+
+LQ_DEVICE int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // Code word (element i at bits 4i..4i+3) -> 4 bf16 pairs (128 + c_2i,
 // 128 + c_2i+1), i.e. natural k order: byte i of the word gives the low
@@ -52,22 +77,33 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
                                                        const float *__restrict__ scales,
                                                        const float *__restrict__ zeros, int group,
                                                        float *__restrict__ y) {
-    __shared__ uint16_t a_lds[2][BM][LDS_ROW];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int l16 = lane & 15, kq = lane >> 4;
+
+    // tile of this block
+    const int nt_count = (n + BN - 1) / BN, mt_count = (m + BM - 1) / BM;
+    int tn, tm;
+    if ((nt_count & 7) == 0) {
+        const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+        tn = xcd * (nt_count >> 3) + idx / mt_count;
+        tm = idx % mt_count;
+    } else {
+        tn = blockIdx.x % nt_count;
+        tm = blockIdx.x / nt_count;
+    }
+    const int n0 = tn * BN, m0 = tm * BM;
     const int ng = k / group;
     const int ngroups = k / GK;
 
-    // activation rows of this block; rows past m read zeros
-    const int rows_m = min(BM, m - m0);
-    const auto rx = make_rsrc(x + (int64_t)m0 * k, (uint32_t)rows_m * (uint32_t)k * 2);
-    // code rows of this block; rows past n read zeros
-    const int rows_n = min(BN, n - n0);
+    // rows past m and code columns past n read zeros, or leave stale bytes,
+    // in LDS; they only feed outputs that are never stored
+    const int rows_m = min(BM, m - m0), rows_n = min(BN, n - n0);
     const uint32_t row_bytes = (uint32_t)k / 2;
+    const auto rx = make_rsrc(x + (int64_t)m0 * k, (uint32_t)rows_m * (uint32_t)k * 2);
     const auto rc = make_rsrc(codes + (int64_t)n0 * row_bytes, (uint32_t)rows_n * row_bytes);
     const auto rs = make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows_n * ng * 4);
     const auto rz = make_rsrc(SYM ? scales : zeros + (int64_t)n0 * ng, SYM ? 0u : (uint32_t)rows_n * ng * 4);
@@ -76,21 +112,58 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagicPair));
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4{kOnePair, kOnePair, kOnePair, kOnePair});
 
-    // staging: thread t moves 16-byte chunks t + 256 i (i = 0..7) of the
-    // 128 x 128 activation tile: row t / 16 + 16 i, columns 8 (t % 16) + [0, 8)
-    const int st_row = tid >> 4, st_col = (tid & 15) * 8;
-    u32x4 stage[8];
-    auto load_stage = [&](int g) {
+    // This wave's loads: 1 KB pieces q = kPiecesPerWave * wave + i of a slot.
+    // Pieces 0..31: activation rows 4 q .. + 3; lane l writes LDS bytes 16 l
+    // of the piece: row 4 q + l / 16, chunk slot l % 16, holding the row's
+    // logical chunk (l % 16) ^ (row & 15). Pieces 32..39: code columns
+    // 16 p .. + 15 (p = q - 32); lane l: column 16 p + l / 4, chunk slot l % 4,
+    // holding logical chunk (l % 4) ^ swz(column).
+    uint32_t src_off[kPiecesPerWave];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            stage[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rx, ((uint32_t)(st_row + 16 * i) * (uint32_t)k + g * GK + st_col) * 2, 0, 0);
-    };
-    auto store_stage = [&](int buf) {
+    for (int i = 0; i < kPiecesPerWave; ++i) {
+        const int q = kPiecesPerWave * wave + i;
+        if (q < kXBytes / 1024) {
+            const int row = 4 * q + (lane >> 4);
+            src_off[i] = (uint32_t)row * (uint32_t)k * 2 + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+        } else {
+            const int col = 16 * (q - kXBytes / 1024) + (lane >> 2);
+            src_off[i] = (uint32_t)col * row_bytes + 16u * (uint32_t)((lane & 3) ^ swz(col));
+        }
+    }
+    auto issue = [&](int g) {
+        uint8_t *slot = ring[g % kStages];
+        const bool in = g < ngroups;  // later steps only keep the load count uniform
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4 *>(&a_lds[buf][st_row + 16 * i][st_col]) = stage[i];
+        for (int i = 0; i < kPiecesPerWave; ++i) {
+            const int q = kPiecesPerWave * wave + i;
+            const bool is_x = q < kXBytes / 1024;  // wave-uniform
+            const uint32_t step_bytes = is_x ? GK * 2 : GK / 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_x ? rx : rc,
+                                                     (__attribute__((address_space(3))) void *)(slot + 1024 * q), 16,
+                                                     in ? src_off[i] + (uint32_t)g * step_bytes : kOutOfRange, 0, 0,
+                                                     0);
+        }
+        // scales (waves 0, 1) or zeros (waves 2, 3) of the group, columns
+        // 64 (wave & 1) + lane; no zeros when symmetric: an empty range
+        const uint32_t gi = (uint32_t)((g * GK) / group);
+        const uint32_t so = (uint32_t)((64 * (wave & 1) + lane) * ng) * 4 + gi * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? rs : rz,
+                                                 (__attribute__((address_space(3))) void *)(slot + kSZOff + 256 * wave),
+                                                 4, in ? so : kOutOfRange, 0, 0, 0);
     };
+
+    // fragment addresses within a slot
+    int a_off[4][4], c_off[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // lane's k = 32 kq + 8 j + [0, 8): logical chunk 4 kq + j
+            a_off[mt][j] = (wm * 64 + mt * 16 + l16) * (GK * 2) + 16 * ((4 * kq + j) ^ l16);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int col = wn * 64 + nt * 16 + l16;
+        c_off[nt] = kXBytes + col * (GK / 2) + 16 * (kq ^ swz(col));
+    }
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -98,27 +171,29 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s);
     for (int g = 0; g < ngroups; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < ngroups) load_stage(g + 1);  // next group's activations, in flight during this one
+        // Step barrier. LDS-write loads are counted by vmcnt only and the
+        // compiler does not track them, so the wait is explicit: this wave's
+        // loads of step g are done once at most (kStages - 2) steps' loads
+        // are younger; after the barrier every wave's are, and every wave has
+        // finished step g - 1, whose slot the issue below refills.
+        asm volatile("s_waitcnt vmcnt(" LQ_GEMM_STR(LQ_GEMM_VM_STEP) ")\n\ts_barrier" ::: "memory");
+        issue(g + kStages - 1);
 
-        // this wave's code words: column wn*64 + nt*16 + l16, k quarter kq of the group
-        u32x4 cw[4];
+        const uint8_t *slot = ring[g % kStages];
+        // scales and zeros of columns wn*64 + nt*16 + l16
         float sc[4], zc[4];
-        const int gi = (g * GK) / group;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const uint32_t col = wn * 64 + nt * 16 + l16;
-            // cached: the same code words are read by every m-block
-            cw[nt] = __builtin_amdgcn_raw_buffer_load_b128(rc, col * row_bytes + g * (GK / 2) + kq * 16, 0, 0);
-            sc[nt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (col * ng + gi) * 4, 0, 0));
-            zc[nt] = SYM ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, (col * ng + gi) * 4, 0, 0));
+            const int col = wn * 64 + nt * 16 + l16;
+            sc[nt] = reinterpret_cast<const float *>(slot + kSZOff)[col];
+            zc[nt] = SYM ? 0.0f : reinterpret_cast<const float *>(slot + kSZOff + BN * 4)[col];
         }
-
+        u32x4 cw[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) cw[nt] = *reinterpret_cast<const u32x4 *>(slot + c_off[nt]);
         f32x4 d[4][4], xg[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -136,8 +211,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8_t aop = *reinterpret_cast<const bf16x8_t *>(
-                    &a_lds[buf][wm * 64 + mt * 16 + l16][kq * 32 + j * 8]);
+                const bf16x8_t aop = *reinterpret_cast<const bf16x8_t *>(slot + a_off[mt][j]);
                 xg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, ones, xg[mt], 0, 0, 0);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
@@ -155,11 +229,10 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
                     acc[mt][nt][v] = __builtin_fmaf(sc[nt], __builtin_fmaf(-c, xg[mt][v], d[mt][nt][v]),
                                                     acc[mt][nt][v]);
         }
-        if (g + 1 < ngroups) {
-            store_stage(buf ^ 1);
-            __syncthreads();
-        }
     }
+    // drain the trailing (out-of-range) LDS-write loads before the block
+    // exits; the builtin also tells the compiler nothing is pending
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // epilogue: lane holds Y[row 4 kq + v][col l16] of each 16 x 16 tile
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -176,13 +249,13 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const W4Args &a, hipStream_t st) {
-    dim3 grid((uint32_t)((a.n + BN - 1) / BN), (uint32_t)((a.m + BM - 1) / BM));
+    const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
     if (a.symmetric)
-        hipLaunchKernelGGL(gemm_w4_kernel<true>, grid, dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k, a.codes,
-                           a.scales, a.zeros, (int)a.group, a.y);
-    else
-        hipLaunchKernelGGL(gemm_w4_kernel<false>, grid, dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k,
+        hipLaunchKernelGGL(gemm_w4_kernel<true>, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k,
                            a.codes, a.scales, a.zeros, (int)a.group, a.y);
+    else
+        hipLaunchKernelGGL(gemm_w4_kernel<false>, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
+                           (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y);
     return hipGetLastError();
 }
 
