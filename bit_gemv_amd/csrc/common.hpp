@@ -52,6 +52,22 @@ LQ_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any resource used here
 constexpr int kNonTemporal = 2;                // buffer-load cache policy: streaming
 
+// INT4 code word (element i at bits 4i..4i+3) -> 4 packed bf16 pairs
+// (128 + c_2i, 128 + c_2i+1), natural k order: byte i of the word gives the
+// low half, byte i of the word shifted right by 4 the high half. A nibble
+// ORed into the mantissa of bf16 128 is exactly 128 + c. `magic` holds the
+// bf16 pair (128, 128) = 0x43004300 (passed in a VGPR so the masking selects
+// v_and_or_b32).
+LQ_DEVICE u32x4 unpack_natural(uint32_t w, uint32_t magic) {
+    const uint32_t w4 = w >> 4;
+    u32x4 p;
+    p.x = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & 0x000F000Fu) | magic;
+    p.y = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & 0x000F000Fu) | magic;
+    p.z = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & 0x000F000Fu) | magic;
+    p.w = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & 0x000F000Fu) | magic;
+    return p;
+}
+
 // Workgroup barrier ordering LDS accesses only. __syncthreads() also
 // releases global memory, which makes each wave wait for all of its
 // outstanding global loads; this one leaves prefetches in flight.

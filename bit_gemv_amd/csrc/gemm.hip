@@ -47,7 +47,6 @@ constexpr int kLoadsPerWave = kPiecesPerWave + 1;               // and one 4-byt
 #define LQ_GEMM_VM_STEP 11
 static_assert(LQ_GEMM_VM_STEP == (kStages - 2) * kLoadsPerWave, "step barrier vmcnt");
 
-constexpr uint32_t kNibPair = 0x000F000Fu;
 constexpr uint32_t kMagicPair = 0x43004300u;  // bf16 pair (128, 128)
 constexpr uint32_t kOnePair = 0x3F803F80u;    // bf16 pair (1, 1)
 // s_waitcnt immediate (gfx9 layout): vmcnt(0), expcnt and lgkmcnt not waited on
@@ -57,19 +56,6 @@ constexpr int kWaitVm0 = 0x0F70;
 #define LQ_GEMM_STR(x) LQ_GEMM_STR2(x)
 
 LQ_DEVICE int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// Code word (element i at bits 4i..4i+3) -> 4 bf16 pairs (128 + c_2i,
-// 128 + c_2i+1), i.e. natural k order: byte i of the word gives the low
-// half, byte i of the word shifted right by 4 gives the high half.
-LQ_DEVICE u32x4 unpack_natural(uint32_t w, uint32_t magic) {
-    const uint32_t w4 = w >> 4;
-    u32x4 p;
-    p.x = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & kNibPair) | magic;
-    p.y = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & kNibPair) | magic;
-    p.z = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & kNibPair) | magic;
-    p.w = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & kNibPair) | magic;
-    return p;
-}
 
 template <bool SYM>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict__ x, int m, int n, int k,

@@ -281,117 +281,144 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restri
 
 // ---------------------------------------------------------------------------
 // MFMA kernel, batch 5..16 (v_mfma_f32_16x16x32_bf16).
-// A = weights (16 rows x 32 k), B = activations (32 k x 16 batch columns,
-// zero beyond the batch), D = 16 rows x 16 columns in fp32. Lane l serves
-// weight row l % 16 and k quarter l / 16: its 16-byte code load covers 32
-// consecutive k, and MFMA step j (0..3) takes code word j, so the four steps
-// of one load cover exactly one 128-wide group. The activation operand uses
-// the same (lane, step) -> k map, re-paired to match the nibble pairs. The
-// four steps accumulate into a fresh tile per group, which is then scaled:
-// acc += s (D_g - (128 + z) X_g), X_g the group's activation sums.
-// Block = 4 waves over RT row tiles of 16 rows; the waves split the groups
-// of k and reduce through LDS.
+// A = weights (16 rows x 32 k), B = activations (32 k x 16 batch columns),
+// D = 16 rows x 16 columns in fp32. Lane l serves weight row l % 16 (A) and
+// batch column l % 16 (B), k quarter l / 16: its 16-byte code load covers 32
+// consecutive k of a 128-wide group, MFMA step j (0..3) takes code word j
+// unpacked in natural k order, and the activation operand of step j is the
+// lane's 8 consecutive bf16 at the same k; the four steps cover the group.
+// Per group the tile D_g and the activation sums X_g (an MFMA against a
+// bf16 ones operand, which lands in the same layout) give
+// acc += s (D_g - (128 + z) X_g). Columns past the batch read a valid batch
+// row and are never stored.
+// A wave owns two row tiles (32 rows, sharing the activation operand) and a
+// contiguous run of gpw groups; the block's waves (up to 16) split k and
+// reduce through LDS. Each group's scales and zeros of the 32 rows come from
+// one 4-byte load per lane and are transposed through the wave's LDS slice.
+// The next group's loads are issued before the current group is computed.
 // ---------------------------------------------------------------------------
-template <int RT, bool SYM>
-__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t *__restrict__ x, int bsz,
-                                                         const uint8_t *__restrict__ codes,
-                                                         const float *__restrict__ scales,
-                                                         const float *__restrict__ zeros, int n, int k,
-                                                         int group, float *__restrict__ y) {
-    __shared__ float red[4][RT][16][17];
+constexpr int kMfmaRows = 32;  // rows per block (and per wave)
+
+template <bool SYM>
+__global__ __launch_bounds__(1024) void gemv_mfma_kernel(const uint16_t *__restrict__ x, int bsz,
+                                                          const uint8_t *__restrict__ codes,
+                                                          const float *__restrict__ scales,
+                                                          const float *__restrict__ zeros, int n, int k,
+                                                          int group, int gpw, float *__restrict__ y) {
+    __shared__ float red[16][2][16][17];
+    __shared__ __attribute__((aligned(16))) float sz_lds[16][64];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int lr = lane & 15;   // weight row within a tile (A operand) / batch column (B operand)
-    const int kq = lane >> 4;   // k quarter of the group
-    const int row_base = blockIdx.x * (16 * RT);
-    const int ng128 = k / 128;  // 128-wide sub-groups (a group is a multiple of 128)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int row0 = blockIdx.x * kMfmaRows;
     const int ng = k / group;
-    const int64_t row_bytes = k / 2;
-    const bool bvalid = lr < bsz;
-    const uint16_t *xrow = x + (int64_t)(bvalid ? lr : 0) * k;
+    const int ng128 = k / 128;
+    const uint32_t row_bytes = (uint32_t)k / 2;
+    const int rows_here = min(kMfmaRows, n - row0);
+    // one code descriptor per 16-row tile (rows past n read zeros)
+    const auto rc0 = make_rsrc(codes + (int64_t)row0 * row_bytes, (uint32_t)min(16, rows_here) * row_bytes);
+    const auto rc1 = make_rsrc(codes + (int64_t)(row0 + 16) * row_bytes,
+                               (uint32_t)max(0, rows_here - 16) * row_bytes);
+    const auto rsc = make_rsrc(scales + (int64_t)row0 * ng, (uint32_t)rows_here * ng * 4);
+    const auto rz = make_rsrc(SYM ? scales : zeros + (int64_t)row0 * ng, SYM ? 0u : (uint32_t)rows_here * ng * 4);
+    // activation row of this lane's batch column (columns past the batch
+    // reuse a valid row; their outputs are dropped)
+    const uint16_t *xrow = x + (int64_t)min(l16, bsz - 1) * k + 32 * kq;
+    const int g_begin = wave * gpw, g_end = min(ng128, g_begin + gpw);
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4{kOnes, kOnes, kOnes, kOnes});
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
 
-    f32x4 acc[RT];
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    struct GroupLoads {
+        u32x4 cw0, cw1, xv[4];
+        float sz;
+    };
+    // loads of group g; past this wave's run the addresses are clamped to its
+    // last group and the scales read zero, so such a group adds nothing
+    auto issue = [&](int g, GroupLoads &L) {
+        const bool gv = g < g_end;
+        g = min(g, g_end - 1);
+        const uint32_t co = (uint32_t)l16 * row_bytes + (uint32_t)g * 64 + 16u * kq;
+        L.cw0 = __builtin_amdgcn_raw_buffer_load_b128(rc0, co, 0, kNonTemporal);
+        L.cw1 = __builtin_amdgcn_raw_buffer_load_b128(rc1, co, 0, kNonTemporal);
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(xrow + (int64_t)g * 128);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int g = wave; g < ng128; g += 4) {
-        const int kb = g * 128 + kq * 32;  // this lane's 32 k of the group
-        u32x4 cw[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const int row = row_base + t * 16 + lr < n ? row_base + t * 16 + lr : n - 1;
-            cw[t] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(codes + (int64_t)row * row_bytes + kb / 2));
+        for (int j = 0; j < 4; ++j) L.xv[j] = xp[j];
+        // lanes 0..31: scale of row lane; lanes 32..63: zero of row lane - 32
+        const uint32_t so = gv ? (uint32_t)((lane & 31) * ng + (g * 128) / group) * 4 : kOutOfRange;
+        const float sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, lane < 32 ? so : kOutOfRange, 0, 0));
+        const float zv = SYM ? 0.0f
+                             : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, lane >= 32 ? so : kOutOfRange, 0, 0));
+        L.sz = lane < 32 ? sv : zv;
+    };
+    auto compute = [&](const GroupLoads &L) {
+        // scales / zeros of rows 4 kq + v of each tile, via the wave's LDS slice
+        sz_lds[wave][lane] = L.sz;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][4 * kq]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][16 + 4 * kq]);
+        f32x4 z0 = f32x4{0.f, 0.f, 0.f, 0.f}, z1 = z0;
+        if (!SYM) {
+            z0 = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][32 + 4 * kq]);
+            z1 = *reinterpret_cast<const f32x4 *>(&sz_lds[wave][48 + 4 * kq]);
         }
-        // scale / zero of the 4 rows whose outputs this lane holds
-        const int gi = (g * 128) / group;
-        float sc[RT][4], zc[RT][4];
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r0 = row_base + t * 16 + kq * 4 + i;
-                const int row = r0 < n ? r0 : n - 1;
-                sc[t][i] = scales[(int64_t)row * ng + gi];
-                zc[t][i] = SYM ? 0.0f : zeros[(int64_t)row * ng + gi];
-            }
-        // activations: 32 k of batch column lr, paired like the nibbles
-        uint32_t xp[16];
-        {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow + kb);
-            u32x4 xv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xv[j] = src[j];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pair_x(xv[j], &xp[4 * j]);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) xp[j] = bvalid ? xp[j] : 0u;
-        }
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[t][i] = row_base + t * 16 + kq * 4 + i < n ? sc[t][i] : 0.0f;
-                zc[t][i] = SYM ? 136.0f : 128.0f + zc[t][i];
-            }
-        // X_g for column lr: sum over the 4 lanes (k quarters) of that column
-        float xs = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) xs = dot2_bf16(xp[j], kOnes, xs);
-        xs += __shfl_xor(xs, 16, 64);
-        xs += __shfl_xor(xs, 32, 64);
-        bf16x8_t bop[4];
+        // the next group's writes must not pass these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 d0 = f32x4{0.f, 0.f, 0.f, 0.f}, d1 = d0, xg = d0;
+        const uint32_t w0[4] = {L.cw0.x, L.cw0.y, L.cw0.z, L.cw0.w};
+        const uint32_t w1[4] = {L.cw1.x, L.cw1.y, L.cw1.z, L.cw1.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            u32x4 v = u32x4{xp[4 * j], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]};
-            bop[j] = __builtin_bit_cast(bf16x8_t, v);
+            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, L.xv[j]);
+            const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, unpack_natural(w0[j], magic));
+            const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, unpack_natural(w1[j], magic));
+            xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bop, xg, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bop, d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bop, d1, 0, 0, 0);
         }
+        // lane holds D[row 4 kq + v][col l16]; X_g of column l16 in every v
+        const float c = 128.0f;
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint32_t words[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t p[4];
-                unpack_word(words[j], p, kMagic);
-                const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, u32x4{p[0], p[1], p[2], p[3]});
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[j], d, 0, 0, 0);
-            }
-            // lane holds D[row = 4 kq + i][col = lr]; the column's X_g is xs
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[t][i] = __builtin_fmaf(sc[t][i], __builtin_fmaf(-zc[t][i], xs, d[i]), acc[t][i]);
+        for (int v = 0; v < 4; ++v) {
+            const float c0 = SYM ? 136.0f : c + z0[v];
+            const float c1 = SYM ? 136.0f : c + z1[v];
+            acc0[v] = __builtin_fmaf(s0[v], __builtin_fmaf(-c0, xg[v], d0[v]), acc0[v]);
+            acc1[v] = __builtin_fmaf(s1[v], __builtin_fmaf(-c1, xg[v], d1[v]), acc1[v]);
+        }
+    };
+
+    if (g_begin < g_end) {
+        // two groups per trip, both computed unconditionally: a conditional
+        // exit between a load and its use would let the compiler sink the
+        // prefetch to the use
+        GroupLoads A, Bn;
+        issue(g_begin, A);
+        for (int g = g_begin; g < g_end; g += 2) {
+            issue(g + 1, Bn);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(A);
+            issue(g + 2, A);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(Bn);
         }
     }
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][t][kq * 4 + i][lr] = acc[t][i];
+    for (int v = 0; v < 4; ++v) {
+        red[wave][0][4 * kq + v][l16] = acc0[v];
+        red[wave][1][4 * kq + v][l16] = acc1[v];
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < RT * 256; e += 256) {
+    for (int e = threadIdx.x; e < 2 * 256; e += blockDim.x) {
         const int t = e >> 8, rr = (e >> 4) & 15, col = e & 15;
-        const float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
-        const int row = row_base + t * 16 + rr;
+        float v = 0.0f;
+        for (int w = 0; w < nwaves; ++w) v += red[w][t][rr][col];
+        const int row = row0 + t * 16 + rr;
         if (row < n && col < bsz) y[(int64_t)col * n + row] = v;
     }
 }
@@ -423,12 +450,19 @@ static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
     return blocks8 >= 512 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
 }
 
+// Waves per block: enough to put about 2048 waves on the chip (8 per CU),
+// 4 to 16, and no more than there are groups; then the runs are balanced.
 template <bool SYM>
 static hipError_t launch_mfma(const W4Args &a, hipStream_t st) {
-    constexpr int RT = 2;
-    const int64_t blocks = (a.n + 16 * RT - 1) / (16 * RT);
-    hipLaunchKernelGGL((gemv_mfma_kernel<RT, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x, (int)a.m,
-                       a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, a.y);
+    const int64_t blocks = (a.n + kMfmaRows - 1) / kMfmaRows;
+    const int ng128 = (int)(a.k / 128);
+    int wpb = 4;
+    while (wpb < 16 && blocks * wpb < 2048) wpb *= 2;
+    wpb = wpb < ng128 ? wpb : ng128;
+    const int gpw = (ng128 + wpb - 1) / wpb;
+    wpb = (ng128 + gpw - 1) / gpw;
+    hipLaunchKernelGGL((gemv_mfma_kernel<SYM>), dim3((uint32_t)blocks), dim3(64 * wpb), 0, st, a.x, (int)a.m,
+                       a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, gpw, a.y);
     return hipGetLastError();
 }
 

@@ -49,6 +49,22 @@ def test_batches(b, sym):
     _case(203, 4096 + 640, b, sym, seed=b)
 
 
+@pytest.mark.parametrize("b", [5, 16])
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(4096 + 17, 11008), (12288, 4096), (33, 128), (1000, 128 * 37), (64, 28672)])
+def test_mfma_batches(n, k, b, sym):
+    """Batches 5..16 on the matrix-core kernel: ragged row tiles, one group
+    per wave, uneven group runs, long rows split 16 ways."""
+    _case(n, k, b, sym, seed=n % 89 + b)
+
+
+@pytest.mark.parametrize("b", [6, 16])
+@pytest.mark.parametrize("group", [256, 1024, "k"])
+def test_mfma_larger_groups(b, group):
+    k = 4096
+    _case(300, k, b, False, group=k if group == "k" else group, seed=b)
+
+
 @pytest.mark.parametrize("group", [256, "k"])
 def test_larger_groups(group):
     k = 2048
