@@ -182,9 +182,10 @@ def cpu_baseline(wl, B, min_seconds: float = 10.0) -> dict:
             "quantize_sample": f"same linears, {q_bytes / 1e9:.2f} GB in {t_q:.1f} s"}
 
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o kt -- "
-             "python3 bench.py --steps 5 --warmup 2 --skip-cpu")
-PMC_CMD = "rocprofv3 --pmc {c} -d gpurun_out/prof_{d} -o {d} -- python3 bench.py --counter-pass"
+# $REPO is the repository root; rocprofv3 runs from /tmp (export TMPDIR=/tmp)
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_kt -o kt -- "
+             "python3 $REPO/bench.py --steps 5 --warmup 2 --skip-cpu")
+PMC_CMD = "rocprofv3 --pmc {c} -d $REPO/gpurun_out/prof_{d} -o {d} -- python3 $REPO/bench.py --counter-pass"
 
 
 def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
@@ -200,7 +201,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
     rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration), grid_x "
                      "from kernels group by name, grid_x order by sum(duration) desc").fetchall()
     lines = ["# Kernel trace: Llama-70B-shaped decode benchmark (bench.py default run, 5 steps)", "",
-             f"Command (from the repository root on the GPU box): `cd /tmp && {TRACE_CMD}`", "",
+             f"Command: `cd /tmp && export TMPDIR=/tmp && {TRACE_CMD}` ($REPO = repository root)", "",
              "Durations from rocprofv3 --kernel-trace, microseconds. `grid` is the number of work-items.", "",
              "| kernel | grid | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
     dom_avg = None
@@ -248,13 +249,13 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
                                 "fetch_factor": round(ffac, 5), "write_factor": round(wfac, 5)},
            "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes_per_launch": alg,
            "traffic_over_algorithmic": round(hbm / alg, 4),
-           "commands": [f"cd /tmp && {PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
-                        f"cd /tmp && {PMC_CMD.format(c='WRITE_SIZE', d='write')}"]}
+           "commands": [f"cd /tmp && export TMPDIR=/tmp && {PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
+                        f"cd /tmp && export TMPDIR=/tmp && {PMC_CMD.format(c='WRITE_SIZE', d='write')}"]}
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     md = ["# HBM traffic of the batch-1 W4A16 GEMV (fused gate|up, 57344 x 8192)", "",
-          "Commands (from the repository root on the GPU box):", "",
+          "Commands ($REPO = repository root):", "",
           *[f"- `{cmd}`" for cmd in out["commands"]], "",
           "Each pass runs torch's copy of 1 GiB three times (calibration) and the GEMV once on each of 8 "
           "address-distinct weight buffers. Counters are per dispatch, in KiB.", "",
