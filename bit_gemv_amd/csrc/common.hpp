@@ -44,6 +44,32 @@ LQ_DEVICE float team_min(float v) {
     return v;
 }
 
+// DPP lane moves inside rows of 16 lanes (gfx9 DPP control codes)
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16 lanes
+
+template <int CTRL>
+LQ_DEVICE float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max / min over each aligned row of 16 lanes, result in every lane: the
+// partners l ^ 15, l ^ 7, l ^ 2, l ^ 1 together reach all 16 lanes.
+LQ_DEVICE float row16_max(float v) {
+    v = fmaxf(v, dpp_move<kDppMirror>(v));
+    v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_move<kDppXor2>(v));
+    return fmaxf(v, dpp_move<kDppXor1>(v));
+}
+LQ_DEVICE float row16_min(float v) {
+    v = fminf(v, dpp_move<kDppMirror>(v));
+    v = fminf(v, dpp_move<kDppHalfMirror>(v));
+    v = fminf(v, dpp_move<kDppXor2>(v));
+    return fminf(v, dpp_move<kDppXor1>(v));
+}
+
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3).
 // Loads whose offset falls outside return zeros instead of faulting.
 LQ_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {

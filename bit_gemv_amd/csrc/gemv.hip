@@ -61,17 +61,6 @@ LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) 
     return acc;
 }
 
-// DPP lane moves inside rows of 16 lanes (gfx9 DPP control codes)
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8 lanes
-constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16 lanes
-
-template <int CTRL>
-LQ_DEVICE float dpp_move(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 // Transposed exchange across lane halves of width 32 (or 16): afterwards the
 // lanes of the lower half hold a + (partner's a), those of the upper half
 // b + (partner's b). v_permlane{32,16}_swap trades the upper half of its

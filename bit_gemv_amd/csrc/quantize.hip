@@ -51,16 +51,78 @@ LQ_DEVICE void scale_zero(float a, float mn, float mx, float &s, float &z) {
     }
 }
 
-// Integer code of one element (before the INT4 symmetric +8 offset).
+// Integer code of one element from its quotient x / s (before the INT4
+// symmetric +8 offset).
 template <int BITS, bool SYM>
-LQ_DEVICE int code_of(float x, float s, float z) {
+LQ_DEVICE int code_of_quotient(float qd, float z) {
     if (SYM) {
         const float qmax = (float)((1 << (BITS - 1)) - 1);
-        return (int)clamp_code(rintf(x / s), -qmax, qmax);
+        return (int)clamp_code(rintf(qd), -qmax, qmax);
     } else {
         const float levels = (float)((1 << BITS) - 1);
-        float r = rintf(x / s) + z;  // round first, then add z
+        const float r = rintf(qd) + z;  // round first, then add z
         return (int)clamp_code(r, 0.0f, levels);
+    }
+}
+
+// fp32 quotient a / b from y = RN(1 / b) and FMA corrections (Markstein's
+// division; Muller et al., Handbook of Floating-Point Arithmetic, division
+// with a fused multiply-add): the first correction leaves q1 within one ulp
+// of a / b, and for such a q1 the step RN(q1 + (a - b q1) y), with the
+// residual exact, is RN(a / b), the IEEE quotient. That holds while every
+// intermediate is normal and finite. The fast path of a group (magnitudes at
+// most 2^59) uses it for
+//  * the scale, range or absmax (at least 1e-8) over the level count: all
+//    intermediates are at least about 1e-8 * 2^-24, hence normal;
+//  * quotients that are then rounded to an integer, with divisor s in
+//    [1e-8 / 255, 2^60 / 7]: a quotient of magnitude 1/2 or more has
+//    |a| >= s / 2, so its residual is normal too; smaller ones round to
+//    zero under either path.
+LQ_DEVICE float div_rn(float a, float b, float y) {
+    const float q0 = a * y;
+    const float r0 = __builtin_fmaf(-q0, b, a);
+    const float q1 = __builtin_fmaf(r0, y, q0);
+    const float r1 = __builtin_fmaf(-q1, b, a);
+    return __builtin_fmaf(r1, y, q1);
+}
+
+// Fast path of a group: every magnitude at most 2^59. Then s lies in
+// [1e-8 / 255, 2^60 / 7] (range or absmax floored at 1e-8), every quotient
+// x / s, -mn / s and range / levels meets div_rn's conditions, and nothing
+// is infinite or NaN, so the clamp may use v_med3.
+constexpr float kFastMax = 5.76460752303423488e+17f;  // 2^59
+LQ_DEVICE bool fast_group(float amax) { return amax <= kFastMax; }
+
+// Scale, zero and reciprocal scale on the fast path: the same values as
+// scale_zero (divisions by the level count through div_rn with the constant
+// RN(1 / levels)).
+template <int BITS, bool SYM>
+LQ_DEVICE void scale_zero_fast(float a, float mn, float mx, float &s, float &z, float &y) {
+    if (SYM) {
+        constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+        const float am = a < kFloor ? kFloor : a;
+        s = div_rn(am, qmax, 1.0f / qmax);
+        y = 1.0f / s;
+        z = 0.0f;
+    } else {
+        constexpr float levels = (float)((1 << BITS) - 1);
+        float range = mx - mn;
+        range = range < kFloor ? kFloor : range;
+        s = div_rn(range, levels, 1.0f / levels);
+        y = 1.0f / s;
+        z = rintf(div_rn(-mn, s, y)) + 0.0f;  // "+ 0.0f": -0 -> +0
+    }
+}
+
+// Code from a quotient on the fast path (finite values: med3 = clamp).
+template <int BITS, bool SYM>
+LQ_DEVICE int code_fast(float qd, float z) {
+    if (SYM) {
+        constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+        return (int)__builtin_amdgcn_fmed3f(rintf(qd), -qmax, qmax);
+    } else {
+        constexpr float levels = (float)((1 << BITS) - 1);
+        return (int)__builtin_amdgcn_fmed3f(rintf(qd) + z, 0.0f, levels);
     }
 }
 
@@ -108,43 +170,69 @@ LQ_DEVICE void store8(uint8_t *__restrict__ codes, int64_t elem, const int q[8])
     }
 }
 
-// group == 128: a team of 16 lanes owns one group, 8 elements (16 bytes of
-// bf16) per lane. Groups tile the rows contiguously, so group index g covers
-// elements [128 g, 128 g + 128) of the flattened matrix and its scale sits at
+constexpr int kGroupsPerTeam = 4;  // measured on MI355X
+
+// group == 128: a team of 16 lanes owns a group, 8 elements (16 bytes of
+// bf16) per lane, and each team takes GPT groups. A block's 16 GPT groups are
+// contiguous and its load i covers groups 16 i .. 16 i + 15 of them (1 KB per
+// wave, coalesced); all GPT loads are issued before any group is computed.
+// Groups tile the rows contiguously, so group index g covers elements
+// [128 g, 128 g + 128) of the flattened matrix and its scale sits at
 // scales[g].
-template <int BITS, bool SYM, bool CS>
+template <int BITS, bool SYM, bool CS, int GPT>
 __global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restrict__ w,
                                                           int64_t ngroups, int64_t k,
                                                           const float *__restrict__ cs,
                                                           uint8_t *__restrict__ codes,
                                                           float *__restrict__ scales,
                                                           float *__restrict__ zeros) {
-    const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int team = threadIdx.x >> 4;
     const int l = threadIdx.x & 15;
-    if (g >= ngroups) return;  // the whole 16-lane team leaves together
-    const int64_t elem = g * 128 + l * 8;
-    float x[8];
-    load8<CS, true>(w, cs, elem, CS ? elem % k : 0, x);
-    GroupStats<SYM> st;
-    st.init();
+    const int64_t g0 = (int64_t)blockIdx.x * (16 * GPT) + team;
+    float x[GPT][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.add(x[i]);
-    float a = 0.f, mn = 0.f, mx = 0.f;
-    if (SYM) {
-        a = team_max<16>(st.a);
-    } else {
-        mn = team_min<16>(st.mn);
-        mx = team_max<16>(st.mx);
+    for (int i = 0; i < GPT; ++i) {
+        const int64_t g = g0 + 16 * i;
+        if (g < ngroups) {  // team-uniform
+            const int64_t elem = g * 128 + l * 8;
+            load8<CS, true>(w, cs, elem, CS ? elem % k : 0, x[i]);
+        }
     }
-    float s, z;
-    scale_zero<BITS, SYM>(a, mn, mx, s, z);
-    int q[8];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = code_of<BITS, SYM>(x[i], s, z);
-    store8<BITS, SYM>(codes, elem, q);
-    if (l == 0) {
-        scales[g] = s;
-        if (!SYM) zeros[g] = z;
+    for (int i = 0; i < GPT; ++i) {
+        const int64_t g = g0 + 16 * i;
+        if (g >= ngroups) break;  // team-uniform; later groups are past the end too
+        const int64_t elem = g * 128 + l * 8;
+        GroupStats<SYM> st;
+        st.init();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.add(x[i][j]);
+        float a = 0.f, mn = 0.f, mx = 0.f;
+        if (SYM) {
+            a = row16_max(st.a);
+        } else {
+            mn = row16_min(st.mn);
+            mx = row16_max(st.mx);
+        }
+        float s, z;
+        int q[8];
+        // the 16-lane team takes one branch: it shares the extremes
+        if (fast_group(SYM ? a : fmaxf(-mn, mx))) {
+            float y;
+            scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+        } else {
+            scale_zero<BITS, SYM>(a, mn, mx, s, z);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][j] / s, z);
+        }
+        store8<BITS, SYM>(codes, elem, q);
+        if (l == 0) {
+            scales[g] = s;
+            if (!SYM) zeros[g] = z;
+        }
     }
 }
 
@@ -189,8 +277,12 @@ __global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restri
         mn = fminf(fminf(red[1][0], red[1][1]), fminf(red[1][2], red[1][3]));
         mx = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
     }
-    float s, z;
-    scale_zero<BITS, SYM>(a, mn, mx, s, z);
+    float s, z, y = 0.0f;
+    const bool fast = fast_group(SYM ? a : fmaxf(-mn, mx));  // block-uniform
+    if (fast)
+        scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
+    else
+        scale_zero<BITS, SYM>(a, mn, mx, s, z);
     for (int64_t e = t * 8; e < group; e += 2048) {
         float x[8];
         const u32x4 v = *reinterpret_cast<const u32x4 *>(w + base + e);
@@ -201,8 +293,13 @@ __global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restri
             for (int i = 0; i < 8; ++i) x[i] = x[i] * cs[col + i];
         }
         int q[8];
+        if (fast) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = code_of<BITS, SYM>(x[i], s, z);
+            for (int i = 0; i < 8; ++i) q[i] = code_fast<BITS, SYM>(div_rn(x[i], s, y), z);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = code_of_quotient<BITS, SYM>(x[i] / s, z);
+        }
         store8<BITS, SYM>(codes, base + e, q);
     }
     if (t == 0) {
@@ -253,8 +350,8 @@ template <int BITS, bool SYM, bool CS>
 static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
     const int64_t ngroups = a.n * (a.k / a.group);
     if (a.group == 128) {
-        const int64_t blocks = (ngroups * 16 + 255) / 256;
-        hipLaunchKernelGGL((quant_g128_kernel<BITS, SYM, CS>), dim3((uint32_t)blocks), dim3(256), 0, st,
+        const int64_t blocks = (ngroups + 16 * kGroupsPerTeam - 1) / (16 * kGroupsPerTeam);
+        hipLaunchKernelGGL((quant_g128_kernel<BITS, SYM, CS, kGroupsPerTeam>), dim3((uint32_t)blocks), dim3(256), 0, st,
                            a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
     } else {
         hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS>), dim3((uint32_t)ngroups), dim3(256), 0, st,
