@@ -105,6 +105,46 @@ def test_every_finite_bf16_value(sym, shuffle):
     _run(h, 8, sym, 128)
 
 
+def _near_tie_groups(bits, sym, want, seed):
+    """Groups (bf16, 128 wide) chosen from a large random pool because some
+    element's IEEE fp32 quotient x / s lies closest to a rounding tie k + 1/2
+    relative to its size: there a quotient one ulp off would change a code.
+    s, z follow the definition in fp32 (numpy division is IEEE)."""
+    rng = np.random.default_rng(seed)
+    pool = 1 << 16
+    # magnitudes from 2^-20 to 2^20 and shifted ranges, so that s, z and the
+    # quotients spread over many binades (asymmetric groups away from zero)
+    scale = np.exp2(rng.uniform(-20, 20, (pool, 1)))
+    shift = rng.uniform(-3, 3, (pool, 1)) * (0 if sym else 1)
+    w = f32_to_bf16_bits((rng.standard_normal((pool, 128)) + shift) * scale)
+    x = bf16_bits_to_f32(w).astype(np.float32)
+    if sym:
+        qmax = np.float32((1 << (bits - 1)) - 1)
+        s = np.maximum(np.abs(x).max(axis=1, keepdims=True), np.float32(1e-8)) / qmax
+    else:
+        levels = np.float32((1 << bits) - 1)
+        mn, mx = x.min(axis=1, keepdims=True), x.max(axis=1, keepdims=True)
+        s = np.maximum(mx - mn, np.float32(1e-8)) / levels
+    q = (x / s.astype(np.float32)).astype(np.float32)
+    d = np.abs(np.abs(q - np.floor(q)) - np.float32(0.5))
+    ulps = d / np.spacing(np.abs(q).astype(np.float32))
+    exact = (d == 0).any(axis=1)
+    near = np.where(d == 0, np.inf, ulps).min(axis=1)  # closest miss, in ulps
+    order = np.argsort(near)
+    best = np.concatenate([order[: want - want // 4], np.flatnonzero(exact)[: want // 4]])
+    best = np.concatenate([best, order[want - want // 4: want - want // 4 + (want - best.size)]])
+    return w[best]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("sym", [False, True])
+def test_quotients_next_to_rounding_ties(bits, sym):
+    """Codes where x / s sits within a few ulps of k + 1/2 must follow the
+    IEEE quotient exactly (the kernel divides with FMA corrections)."""
+    w = _near_tie_groups(bits, sym, 2048, seed=bits * 2 + sym)
+    _run(w.reshape(-1, 8 * 128), bits, sym, 128)
+
+
 def test_empty_matrix_is_noop():
     w = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
     pw = bg.quantize_groupwise(w, 4, True, 128)
