@@ -40,6 +40,7 @@ CXXFLAGS = [
 EXTRA = {
     "w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -51,10 +51,13 @@ def test_batches(b, sym):
 
 @pytest.mark.parametrize("b", [5, 16])
 @pytest.mark.parametrize("sym", [False, True])
-@pytest.mark.parametrize("n,k", [(4096 + 17, 11008), (12288, 4096), (33, 128), (1000, 128 * 37), (64, 28672)])
+@pytest.mark.parametrize("n,k", [(4096 + 17, 11008), (12288, 4096), (33, 128), (1000, 128 * 37), (64, 28672),
+                                 (12288 + 5, 2048 + 128), (16384 + 33, 4096 + 384)])
 def test_mfma_batches(n, k, b, sym):
-    """Batches 5..16 on the matrix-core kernel: ragged row tiles, one group
-    per wave, uneven group runs, long rows split 16 ways."""
+    """Batches 5..16 on the matrix-core kernels: the LDS-ring kernel (n up to
+    12288: ragged 16-row tiles, a half last 256-wide stage, waves with no
+    stage) and the register-streaming kernel for taller matrices (ragged
+    tiles, uneven group runs)."""
     _case(n, k, b, sym, seed=n % 89 + b)
 
 
