@@ -414,62 +414,68 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(const uint16_t *__restr
 
 // ---------------------------------------------------------------------------
 // Ring kernel, batch 5..16 (v_mfma_f32_16x16x32_bf16, operands through LDS).
-// A block's 4 waves share a tile of 16 RT weight rows and split k into
+// A block's 4 waves share a tile of 16 weight rows and split k into
 // 256-wide stages round-robin. Each wave streams its stages into a private
-// LDS ring (kRingSlots slots) with buffer loads in the LDS-write form: the
-// tile's codes (whole 128-byte lines of every row), the 16 batch rows of
-// activations (512 bytes each; rows past the batch read zeros) and the two
-// groups' scales and zeros of every row. It reads MFMA fragments from LDS:
+// LDS ring with buffer loads in the LDS-write form: the tile's codes (whole
+// 128-byte lines of every row), XR (8 or 16) batch rows of activations (512
+// bytes each; rows past the batch read zeros) and the two groups' scales and
+// zeros of every row. Slots per wave: as many as fit in kRingWaveBytes
+// (3 for XR = 16, 5 for XR = 8), so 1 or 3 stages stay in flight beyond the
+// one being computed. It reads MFMA fragments from LDS:
 // A = 16 rows x 32 k of codes (lane row l % 16, k quarter l / 16, natural
 // unpack, one 16-byte read covers a group's four k-steps), B = 32 k x 16
 // batch columns of activations. Per group the tile D_g and the activation
 // sums X_g (an MFMA against a bf16 ones operand) give
 // acc += s (D_g - (128 + z) X_g). The waves never wait for each other inside
 // the loop (only for their own loads); they reduce through LDS at the end.
-// LDS layout of a slot: codes [RT][16 rows][128 B], 16-byte chunk c of row r
-// stored at c ^ ((r >> 1) & 7); activations [16 rows][512 B], chunk c of row
-// r at c ^ r; scales, then zeros, [RT][64] fp32 with entry 16 g + row for
-// group g of the stage (entries 32..63 unused). With these
-// the 16 rows (columns) of one fragment read fall in distinct banks.
+// LDS layout of a slot: codes [16 rows][128 B], 16-byte chunk c of row r
+// stored at c ^ ((r >> 1) & 7); activations [XR rows][512 B], chunk c of row
+// r at c ^ r (batch column b reads row b % XR; columns past the batch are
+// never stored); scales, then zeros, [64] fp32 with entry 16 g + row for
+// group g of the stage (entries 32..63 unused). With these the 16 rows
+// (columns) of one fragment read fall in distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int kRingSlots = 3;
-// (kRingSlots - 2) stages of loads, symmetric / asymmetric
-#define LQ_GEMV_RING_VM_1S 11
-#define LQ_GEMV_RING_VM_1A 12
 constexpr int kRingStageK = 256;
-
-// slot layout (one 16-row tile); the size does not depend on template
-// parameters (symmetric rings leave the zeros region unused)
+constexpr int kRingWaveBytes = 33792;  // LDS ring of one wave
 constexpr int kRingCodes = 16 * 128;
-constexpr int kRingX = 16 * 512;
-constexpr int kRingS = 256;                                   // scales, then zeros
-constexpr int kRingSlot = kRingCodes + kRingX + 2 * kRingS;
-template <bool SYM>
-constexpr int ring_loads() { return 2 + 8 + (SYM ? 1 : 2); }  // LDS-write loads per stage
+constexpr int kRingS = 256;            // scales, then zeros (symmetric leaves zeros unused)
+constexpr int ring_slot(int xr) { return kRingCodes + xr * 512 + 2 * kRingS; }
+constexpr int ring_slots(int xr) { return kRingWaveBytes / ring_slot(xr); }
+constexpr int ring_loads(int xr, bool sym) { return 2 + xr / 2 + (sym ? 1 : 2); }  // LDS-write loads per stage
+// vmcnt in the stage wait: (slots - 2) stages of younger loads, for
+// XR = 16 / 8 and symmetric / asymmetric (literals: pasted into the asm)
+#define LQ_GEMV_RING_VM_16S 11
+#define LQ_GEMV_RING_VM_16A 12
+#define LQ_GEMV_RING_VM_8S 21
+#define LQ_GEMV_RING_VM_8A 24
 
 #define LQ_GEMV_STR2(x) #x
 #define LQ_GEMV_STR(x) LQ_GEMV_STR2(x)
 
-template <int RT, bool SYM>
+template <int XR, bool SYM>
 __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restrict__ x, int bsz,
                                                          const uint8_t *__restrict__ codes,
                                                          const float *__restrict__ scales,
                                                          const float *__restrict__ zeros, int n, int k,
                                                          int group, float *__restrict__ y) {
-    static_assert(ring_loads<SYM>() * (kRingSlots - 2) == (SYM ? LQ_GEMV_RING_VM_1S : LQ_GEMV_RING_VM_1A),
+    constexpr int kSlot = ring_slot(XR), kSlots = ring_slots(XR), kXP = XR / 2;
+    static_assert(ring_loads(XR, SYM) * (kSlots - 2) ==
+                      (XR == 16 ? (SYM ? LQ_GEMV_RING_VM_16S : LQ_GEMV_RING_VM_16A)
+                                : (SYM ? LQ_GEMV_RING_VM_8S : LQ_GEMV_RING_VM_8A)),
                   "ring vmcnt");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[4][kRingSlots][kRingSlot];
-    __shared__ float red[4][RT][16][17];
+    // one fixed-size array (a lambda capturing an array whose size depends on
+    // a template parameter is dropped from the host compilation)
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kRingWaveBytes];
+    __shared__ float red[4][16][17];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, kq = lane >> 4;
-    const int row0 = blockIdx.x * 16 * RT;
+    const int row0 = blockIdx.x * 16;
     const int ng = k / group;
     const uint32_t row_bytes = (uint32_t)k / 2;
     const int nst = (k + kRingStageK - 1) / kRingStageK;  // stages of this row range
     // descriptors: one per 16-row tile of codes; activations of the batch;
     // scales / zeros of the block's rows (rows past n read zeros)
-    static_assert(RT == 1, "one 16-row tile per block (the ring fills the LDS)");
     const int tile_rows = n - row0 < 16 ? n - row0 : 16;
     const auto rc = make_rsrc(codes + (int64_t)row0 * row_bytes, (uint32_t)tile_rows * row_bytes);
     const auto rx = make_rsrc(x, (uint32_t)bsz * (uint32_t)k * 2);
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     // activation piece q: rows 2 q + l / 32, physical chunk l % 32
     uint32_t x_off[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kXP; ++q) {
         const int xr = 2 * q + (lane >> 5);
         x_off[q] = (uint32_t)xr * (uint32_t)k * 2 + 16u * (uint32_t)((lane & 31) ^ xr);
     }
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     const int sz_grp = (lane >> 4) & 1;
 
     auto issue = [&](int st) {
-        uint8_t *slot = ring[wave][st % kRingSlots];
+        uint8_t *slot = ring + wave * kRingWaveBytes + (st % kSlots) * kSlot;
         const bool in = st < nst;  // later stages only keep the load count uniform
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
                 rc, (__attribute__((address_space(3))) void *)(slot + 1024 * p), 16,
                 in ? c_off[p] + (uint32_t)st * 128 : kOutOfRange, 0, 0, kNonTemporal);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < kXP; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rx, (__attribute__((address_space(3))) void *)(slot + kRingCodes + 1024 * q), 16,
                 in ? x_off[q] + (uint32_t)st * 512 : kOutOfRange, 0, 0, 0);
@@ -515,51 +521,49 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
         const int gi0 = (st * kRingStageK) / group, gi1 = (st * kRingStageK + 128) / group;
         const bool gv = in && lane < 32 && (st * 2 + sz_grp) * 128 < k;
         const uint32_t gi = (uint32_t)(sz_grp ? gi1 : gi0);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const uint32_t so = gv && 16 * t + l16 < rows_here ? (uint32_t)((16 * t + l16) * ng) * 4 + gi * 4
-                                                                : kOutOfRange;
+        const uint32_t so = gv && l16 < rows_here ? (uint32_t)(l16 * ng) * 4 + gi * 4 : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(slot + kRingCodes + XR * 512), 4, so, 0, 0, 0);
+        if (!SYM)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void *)(slot + kRingCodes + kRingX + 256 * t), 4, so, 0, 0, 0);
-            if (!SYM)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rz, (__attribute__((address_space(3))) void *)(slot + kRingCodes + kRingX + kRingS + 256 * t), 4, so,
-                    0, 0, 0);
-        }
+                rz, (__attribute__((address_space(3))) void *)(slot + kRingCodes + XR * 512 + kRingS), 4, so, 0, 0, 0);
     };
 
     uint32_t magic;
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4{kOnes, kOnes, kOnes, kOnes});
-    f32x4 acc[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // fragment offsets within a slot
     int a_off[2];  // A of row l16, group h: logical chunk 4 h + kq
 #pragma unroll
     for (int h = 0; h < 2; ++h) a_off[h] = l16 * 128 + 16 * ((4 * h + kq) ^ ((l16 >> 1) & 7));
-    int b_off[2][4];  // B of column l16, group h, step j: logical chunk 16 h + 4 kq + j
+    int b_off[2][4];  // B of column l16 (row l16 % XR), group h, step j: logical chunk 16 h + 4 kq + j
+    const int xrow = l16 % XR;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b_off[h][j] = kRingCodes + l16 * 512 + 16 * ((16 * h + 4 * kq + j) ^ l16);
+        for (int j = 0; j < 4; ++j) b_off[h][j] = kRingCodes + xrow * 512 + 16 * ((16 * h + 4 * kq + j) ^ xrow);
 
     const int my_stages = wave < nst ? (nst - wave + 3) / 4 : 0;
 #pragma unroll
-    for (int i = 0; i < kRingSlots - 1; ++i) issue(wave + 4 * i);
+    for (int i = 0; i < kSlots - 1; ++i) issue(wave + 4 * i);
     for (int i = 0; i < my_stages; ++i) {
         // this wave's loads of stage i are done once at most (slots - 2)
         // stages of younger loads are pending (the compiler does not track
         // LDS-write loads). The slot the issue below refills was last read
         // by stage i - 1, whose fragments this wave has consumed.
-        if (SYM)
-            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_1S) ")" ::: "memory");
+        if (XR == 16 && SYM)
+            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_16S) ")" ::: "memory");
+        else if (XR == 16)
+            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_16A) ")" ::: "memory");
+        else if (SYM)
+            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_8S) ")" ::: "memory");
         else
-            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_1A) ")" ::: "memory");
-        issue(wave + 4 * (i + kRingSlots - 1));
-        const uint8_t *slot = ring[wave][(wave + 4 * i) % kRingSlots];
-        const float *sz = reinterpret_cast<const float *>(slot + kRingCodes + kRingX);
+            asm volatile("s_waitcnt vmcnt(" LQ_GEMV_STR(LQ_GEMV_RING_VM_8A) ")" ::: "memory");
+        issue(wave + 4 * (i + kSlots - 1));
+        const uint8_t *slot = ring + wave * kRingWaveBytes + ((wave + 4 * i) % kSlots) * kSlot;
+        const float *sz = reinterpret_cast<const float *>(slot + kRingCodes + XR * 512);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             bf16x8_t bop[4];
@@ -568,24 +572,21 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
             f32x4 xg = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bop[j], xg, 0, 0, 0);
+            const u32x4 cw = *reinterpret_cast<const u32x4 *>(slot + a_off[h]);
+            const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+            f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                const u32x4 cw = *reinterpret_cast<const u32x4 *>(slot + t * 2048 + a_off[h]);
-                const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-                f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j)
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, unpack_natural(w[j], magic)),
+                                                            bop[j], d, 0, 0, 0);
+            // rows 4 kq + v of the tile: scales at [16 h + row], zeros 64 entries later
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(&sz[h * 16 + 4 * kq]);
+            f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!SYM) zv = *reinterpret_cast<const f32x4 *>(&sz[64 + h * 16 + 4 * kq]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, unpack_natural(w[j], magic)), bop[j], d, 0, 0, 0);
-                // rows 4 kq + v of the tile: scales at [t][16 h + row], zeros after them
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(&sz[t * 64 + h * 16 + 4 * kq]);
-                f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (!SYM) zv = *reinterpret_cast<const f32x4 *>(&sz[RT * 64 + t * 64 + h * 16 + 4 * kq]);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float c = SYM ? 136.0f : 128.0f + zv[v];
-                    acc[t][v] = __builtin_fmaf(sv[v], __builtin_fmaf(-c, xg[v], d[v]), acc[t][v]);
-                }
+            for (int v = 0; v < 4; ++v) {
+                const float c = SYM ? 136.0f : 128.0f + zv[v];
+                acc[v] = __builtin_fmaf(sv[v], __builtin_fmaf(-c, xg[v], d[v]), acc[v]);
             }
         }
     }
@@ -593,14 +594,12 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     // builtin also tells the compiler nothing is pending
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 layout)
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][t][4 * kq + v][l16] = acc[t][v];
+    for (int v = 0; v < 4; ++v) red[wave][4 * kq + v][l16] = acc[v];
     __syncthreads();
-    for (int e = threadIdx.x; e < RT * 256; e += 256) {
-        const int t = e >> 8, rr = (e >> 4) & 15, col = e & 15;
-        const float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
-        const int row = row0 + t * 16 + rr;
+    {
+        const int rr = threadIdx.x >> 4, col = threadIdx.x & 15;
+        const float v = red[0][rr][col] + red[1][rr][col] + red[2][rr][col] + red[3][rr][col];
+        const int row = row0 + rr;
         if (row < n && col < bsz) y[(int64_t)col * n + row] = v;
     }
 }
@@ -655,8 +654,12 @@ static hipError_t launch_mfma(const W4Args &a, hipStream_t st) {
 template <bool SYM>
 static hipError_t launch_batch(const W4Args &a, hipStream_t st) {
     if (a.n <= 12288 && a.m * a.k * 2 < (int64_t(1) << 32)) {
-        hipLaunchKernelGGL((gemv_ring_kernel<1, SYM>), dim3((uint32_t)((a.n + 15) / 16)), dim3(256), 0, st, a.x,
-                           (int)a.m, a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, a.y);
+        if (a.m <= 8)
+            hipLaunchKernelGGL((gemv_ring_kernel<8, SYM>), dim3((uint32_t)((a.n + 15) / 16)), dim3(256), 0, st, a.x,
+                               (int)a.m, a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, a.y);
+        else
+            hipLaunchKernelGGL((gemv_ring_kernel<16, SYM>), dim3((uint32_t)((a.n + 15) / 16)), dim3(256), 0, st, a.x,
+                               (int)a.m, a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, a.y);
         return hipGetLastError();
     }
     return launch_mfma<SYM>(a, st);
