@@ -1,4 +1,4 @@
-"""CPU oracle for group-wise RTN quantization, W4A16 matmul and SmoothQuant W8A8.
+"""CPU oracle for group-wise RTN quantization, W4A16/W8A16 matmul and SmoothQuant W8A8.
 
 TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. It is the
@@ -16,8 +16,9 @@ hold the pins):
   self-test of the "3.6 Quantization" page, the outlier collapse from its
   "Intuition" section, brute-force nearest-code search on tiny inputs, the
   s/2 error bound, and the constructed half-way ties.
-* ``w4a16_matmul``: the definition y = x W_hat^T, checked against numpy's
-  matmul on the dequantized weights and against closed forms.
+* ``w4a16_matmul`` / ``w8a16_matmul``: the definition y = x W_hat^T,
+  checked against numpy's matmul on the dequantized weights and against
+  closed forms.
 * ``smooth_scale``: the self-test (max|X| = 100, max|W| = 0.01 gives s = 100)
   and the equalised maxima sqrt(max|X| max|W|) of the SmoothQuant section.
 * ``quant_per_token_int8`` / ``w8a8_gemm``: brute force, an int64 numpy
@@ -72,6 +73,7 @@ def _load():
         lib.oracle_quantize_bf16.argtypes = [P, I64, I64, I, I, I64, P, P, P, P]
         lib.oracle_dequantize.argtypes = [P, P, P, I64, I64, I, I, I64, P]
         lib.oracle_w4a16_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I64, P]
+        lib.oracle_weight_only_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I, I64, P]
         lib.oracle_smooth_scale_from_absmax.argtypes = [P, P, I64, F, P]
         lib.oracle_smooth_scale_from_absmax.restype = None
         lib.oracle_smooth_scale.argtypes = [P, I64, P, I64, I64, F, P]
@@ -146,6 +148,19 @@ def w4a16_matmul(x_bf16, codes, scales, zeros, n: int, k: int, symmetric: bool, 
     rc = lib.oracle_w4a16_matmul(_ptr(x), m, _ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.float32)),
                                  _ptr(zc), n, k, int(bool(symmetric)), group, _ptr(y))
     _check(rc, "w4a16_matmul")
+    return y
+
+
+def w8a16_matmul(x_bf16, codes, scales, zeros, n: int, k: int, symmetric: bool, group: int):
+    """W8A16: y[m][n] = sum_k x[m][k] * x_hat[n][k] in fp64 on INT8 codes [n][k]."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    zc = None if symmetric else _c(zeros, np.float32)
+    rc = lib.oracle_weight_only_matmul(_ptr(x), m, _ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.float32)),
+                                       _ptr(zc), n, k, 8, int(bool(symmetric)), group, _ptr(y))
+    _check(rc, "w8a16_matmul")
     return y
 
 

@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain, slow, scalar CPU reference for group-wise RTN
- * quantization, the W4A16 matmul that consumes its packed codes, and the
+ * quantization, the W4A16 and W8A16 matmuls that consume its packed codes, and the
  * SmoothQuant W8A8 path.
  *
  * THIS FILE IS TEST INFRASTRUCTURE. It is the independent checker for the
@@ -244,23 +244,28 @@ int oracle_dequantize(const uint8_t *codes, const float *scales, const float *ze
     return 0;
 }
 
-/* W4A16 matmul ([RL] W4A16: INT4 weights, bf16 activations, weights
- * dequantized and multiplied with the activations, higher-precision
- * accumulation; [RL] linear layer Y = X W^T with W[out, in]):
+/* Weight-only matmul with 16-bit activations ([RL] "storage dtype vs compute
+ * dtype": W4A16 keeps 4-bit weights and bf16 activations, the kernel
+ * dequantizes the weights and multiplies them with the activations,
+ * accumulating at higher precision; [RL] "W/A/KV notation": W8A16 is the
+ * same with 8-bit weights; [RL] linear layer Y = X W^T with W[out, in]):
  *   y[i][r] = sum_j x[i][j] * x_hat[r][j]
- * with x_hat the fp32 dequantized weights above, summed in fp64 in index
- * order. x: bf16 bits [m][k]; y: fp64 [m][n]. */
-int oracle_w4a16_matmul(const uint16_t *x, int64_t m, const uint8_t *codes,
-                        const float *scales, const float *zeros, int64_t n, int64_t k,
-                        int symmetric, int64_t group, double *y)
+ * with x_hat the fp32 dequantized weights above (oracle_dequantize, row by
+ * row), summed in fp64 in index order. x: bf16 bits [m][k]; codes: the
+ * packed storage of `bits` (k / 2 bytes a row for INT4, k for INT8);
+ * y: fp64 [m][n]. */
+int oracle_weight_only_matmul(const uint16_t *x, int64_t m, const uint8_t *codes,
+                              const float *scales, const float *zeros, int64_t n, int64_t k,
+                              int bits, int symmetric, int64_t group, double *y)
 {
-    if (check_args(n, k, 4, group) || m < 0) return -1;
+    if (check_args(n, k, bits, group) || m < 0) return -1;
     float *wrow = (float *)malloc(sizeof(float) * (size_t)k);
     if (!wrow) return -1;
     const int64_t ng = k / group;
+    const int64_t codes_per_row = bits == 4 ? k / 2 : k;
     for (int64_t r = 0; r < n; ++r) {
-        oracle_dequantize(codes + r * (k / 2), scales + r * ng,
-                          symmetric ? NULL : zeros + r * ng, 1, k, 4, symmetric, group, wrow);
+        oracle_dequantize(codes + r * codes_per_row, scales + r * ng,
+                          symmetric ? NULL : zeros + r * ng, 1, k, bits, symmetric, group, wrow);
         for (int64_t i = 0; i < m; ++i) {
             double acc = 0.0;
             for (int64_t j = 0; j < k; ++j)
@@ -270,6 +275,13 @@ int oracle_w4a16_matmul(const uint16_t *x, int64_t m, const uint8_t *codes,
     }
     free(wrow);
     return 0;
+}
+
+int oracle_w4a16_matmul(const uint16_t *x, int64_t m, const uint8_t *codes,
+                        const float *scales, const float *zeros, int64_t n, int64_t k,
+                        int symmetric, int64_t group, double *y)
+{
+    return oracle_weight_only_matmul(x, m, codes, scales, zeros, n, k, 4, symmetric, group, y);
 }
 
 /* SmoothQuant migration strength ([LP] "SmoothQuant"; [CP] SmoothQuant;

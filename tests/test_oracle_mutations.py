@@ -34,6 +34,10 @@ MUTANTS = {
                             "acc += (double)bf16_bits_to_f32(x[j * m + i < m * k ? j * m + i : 0]) * (double)wrow[j];"),
     "matmul_drops_last_element": ("for (int64_t j = 0; j < k; ++j)\n                acc +=",
                                   "for (int64_t j = 0; j + 1 < k; ++j)\n                acc +="),
+    "int8_row_stride_halved": ("const int64_t codes_per_row = bits == 4 ? k / 2 : k;",
+                               "const int64_t codes_per_row = k / 2;"),
+    "int8_sym_read_unsigned": ("return symmetric ? (int32_t)(int8_t)row_codes[j] : (int32_t)row_codes[j];",
+                               "return (int32_t)row_codes[j];"),
     "smooth_inverted": ("s[j] = sqrtf(a) / sqrtf(b);", "s[j] = sqrtf(b) / sqrtf(a);"),
     "smooth_alpha_swapped": ("s[j] = powf(a, alpha) / powf(b, 1.0f - alpha);",
                              "s[j] = powf(a, 1.0f - alpha) / powf(b, alpha);"),

@@ -311,6 +311,58 @@ def test_w4a16_matmul_closed_form():
     assert np.allclose(y[1], 2 * w_hat.astype(np.float64).sum(1), rtol=1e-12)
 
 
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_w8a16_matmul_is_x_times_dequantized_transpose(symmetric):
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(23)
+    n, k, m = 19, 512, 4
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    x = f32_to_bf16_bits(rng.standard_normal((m, k)))
+    codes, s, z = oracle.quantize(w, 8, symmetric, 128)
+    assert codes.size == n * k  # one byte per weight
+    y = oracle.w8a16_matmul(x, codes, s, z, n, k, symmetric, 128)
+    w_hat = oracle.dequantize(codes, s, z, n, k, 8, symmetric, 128).astype(np.float64)
+    ref = bf16_bits_to_f32(x).astype(np.float64) @ w_hat.T
+    assert y.shape == (m, n)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # INT8 is far closer to the unquantized product than INT4 would be
+    full = bf16_bits_to_f32(x).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
+    rel = np.linalg.norm(y - full) / np.linalg.norm(full)
+    assert rel < 0.01
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_w8a16_matmul_hand_built_codes(symmetric):
+    """Codes, scales and zero-points built by hand (not by the quantizer):
+    signed two's-complement bytes for symmetric, unsigned bytes with a
+    zero-point for asymmetric. Power-of-two scales and small-integer
+    activations make every product and sum exact, so the result must equal
+    sum_j x_j (q_j - z) s bit for bit, group by group."""
+    rng = np.random.default_rng(24)
+    n, k, g = 6, 384, 128
+    ng = k // g
+    if symmetric:
+        q = rng.integers(-128, 128, (n, k))
+        codes = (q & 0xFF).astype(np.uint8)
+        z = np.zeros((n, ng), f32)
+    else:
+        q = rng.integers(0, 256, (n, k))
+        codes = q.astype(np.uint8)
+        z = rng.integers(0, 256, (n, ng)).astype(f32)
+    s = (2.0 ** rng.integers(-12, -2, (n, ng))).astype(f32)
+    xi = rng.integers(-8, 9, (2, k))
+    x = (np.float32(1.0) * xi).astype(f32).view(np.uint32)
+    x = (x >> 16).astype(np.uint16)  # small integers are exact in bf16
+    y = oracle.w8a16_matmul(x, codes, s, None if symmetric else z, n, k, symmetric, g)
+    expect = np.zeros((2, n))
+    for i in range(2):
+        for r in range(n):
+            for gi in range(ng):
+                sl = slice(gi * g, (gi + 1) * g)
+                expect[i, r] += float(s[r, gi]) * float(np.dot(xi[i, sl], q[r, sl] - z[r, gi]))
+    assert np.array_equal(y, expect)
+
+
 # --------------------------------------------------------------------------
 # SmoothQuant.
 # --------------------------------------------------------------------------
