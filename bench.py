@@ -57,6 +57,32 @@ def w4_bytes(n: int, k: int, b: int, symmetric: bool, group: int) -> int:
     return n * k // 2 + meta + b * k * 2 + b * n * 4
 
 
+def w8_bytes(n: int, k: int, b: int, symmetric: bool, group: int) -> int:
+    """Algorithmic bytes of one W8A16 product: one code byte per weight, the
+    same scales, activations and outputs as INT4."""
+    return w4_bytes(n, k, b, symmetric, group) + n * k // 2
+
+
+def _graph_ms(fn, reps: int) -> float:
+    """Average ms of one replay of a HIP graph holding fn()'s launches."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / reps
+
+
 def _timed(fn, reps: int = 5) -> float:
     """Average ms of fn() over reps launches, bracketed by HIP events on the
     current stream after one untimed call."""
@@ -84,6 +110,44 @@ def measure_rows(dev, packed, shapes, names, wl) -> dict:
         return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).to(dev)
 
     rows = {}
+    # f3: W8A16 decode, the same layers with INT8 codes, a whole token (every
+    # layer, address-distinct buffers) per graph replay at batch 1, 4 and 16
+    groups = [[0, 1, 2], [3], [4, 5], [6]] if len(wl.linears) == 7 else [[i] for i in range(len(wl.linears))]
+    sym, group = wl.symmetric, wl.group
+    n_sets = min(wl.distinct_layers, 2)
+    src = []
+    for s_ in range(n_sets):
+        mats = []
+        for g in groups:
+            parts = [dev_bf16(wl.weight(s_, i)) for i in g]
+            mats.append(torch.cat(parts, 0) if len(parts) > 1 else parts[0])
+            del parts
+        src.append(mats)
+    packed8 = [[bg.quantize_groupwise(m, 8, sym, group) for m in src[layer % n_sets]] for layer in range(wl.layers)]
+    del src
+    torch.cuda.empty_cache()
+    w8 = {}
+    for b in (1, 4, 16):
+        xs = {k: dev_bf16(wl.activation(k, b)) for k in sorted({k for _, k in shapes})}
+        ys = [torch.empty((b, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+
+        def sweep8():
+            for layer in range(wl.layers):
+                for j, (n, k) in enumerate(shapes):
+                    bg.w8a16_gemv(xs[k], packed8[layer][j], ys[j])
+
+        ms = _graph_ms(sweep8, reps=5)
+        byt = wl.layers * sum(w8_bytes(n, k, b, sym, group) for n, k in shapes)
+        tbs = byt / (ms * 1e-3) / 1e12
+        w8[f"batch{b}"] = {"ms_per_token_step": round(ms, 4), "TBps": round(tbs, 4),
+                           "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4), "bytes": byt}
+        log(f"[bench] w8a16_gemv {wl.name} batch {b}: {ms:.3f} ms/step, {tbs:.3f} TB/s")
+        del xs, ys
+    rows["w8a16_gemv_decode"] = {"workload": wl.name, "layers": wl.layers, "bound": "hbm",
+                                 "quant": f"INT8 {'sym' if sym else 'asym'} G={group}", **w8}
+    del packed8
+    torch.cuda.empty_cache()
+
     # a5: dequantize (fp32 out) of one matrix per layer, across distinct layers
     j = names.index("o") if "o" in names else 0
     n, k = shapes[j]

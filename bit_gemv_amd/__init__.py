@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libquant.so")
 
 LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = range(5)
 
-ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w4a16_gemm",
+ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w8a16_gemv", "w4a16_gemm",
                 "smooth_scale", "quant_per_token_int8", "w8a8_gemm")
 
 
@@ -53,6 +53,7 @@ def load_library(path: Optional[str] = None):
         "quantize_groupwise": [P, I64, I64, I, I, I64, P, P, P, P, P],
         "dequantize_groupwise": [P, P, P, I64, I64, I, I, I64, P, P],
         "w4a16_gemv": [P, I64, P, P, P, I64, I64, I, I64, P, P],
+        "w8a16_gemv": [P, I64, P, P, P, I64, I64, I, I64, P, P],
         "w4a16_gemm": [P, I64, P, P, P, I64, I64, I, I64, P, P],
         "smooth_scale": [P, I64, P, I64, I64, F, P, P],
         "quant_per_token_int8": [P, I64, I64, P, P, P, P],
@@ -149,9 +150,9 @@ def dequantize_groupwise(pw: PackedWeight, out: Optional[torch.Tensor] = None) -
     return out
 
 
-def _w4(name: str, x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor]) -> torch.Tensor:
-    if pw.bits != 4:
-        raise ValueError(f"{name} needs INT4 codes")
+def _wo(name: str, bits: int, x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor]) -> torch.Tensor:
+    if pw.bits != bits:
+        raise ValueError(f"{name} needs INT{bits} codes")
     _need(x, "x", torch.bfloat16)
     m, k = x.shape
     if k != pw.k:
@@ -166,12 +167,17 @@ def _w4(name: str, x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor])
 
 def w4a16_gemv(x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[b][n] = x[b][k] W_hat^T for b <= 16 (fp32 out)."""
-    return _w4("w4a16_gemv", x, pw, y)
+    return _wo("w4a16_gemv", 4, x, pw, y)
+
+
+def w8a16_gemv(x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[b][n] = x[b][k] W_hat^T on INT8 codes for b <= 16 (fp32 out)."""
+    return _wo("w8a16_gemv", 8, x, pw, y)
 
 
 def w4a16_gemm(x: torch.Tensor, pw: PackedWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[m][n] = x[m][k] W_hat^T for any m (fp32 out, bf16 MFMA)."""
-    return _w4("w4a16_gemm", x, pw, y)
+    return _wo("w4a16_gemm", 4, x, pw, y)
 
 
 def smooth_scale(x: torch.Tensor, w: torch.Tensor, alpha: float = 0.5,

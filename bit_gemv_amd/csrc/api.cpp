@@ -96,10 +96,11 @@ lq_status check_meta(const char *fn, int symmetric, const float *scales, const f
     return LQ_OK;
 }
 
-lq_status check_w4(const char *fn, const void *x, int64_t m, const void *codes, const float *scales,
+// Arguments of the weight-only products (INT4 or INT8 codes, bf16 x).
+lq_status check_wo(const char *fn, int bits, const void *x, int64_t m, const void *codes, const float *scales,
                    const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group, const float *y) {
     if (m < 0 || n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size", fn);
-    lq_status st = check_group(fn, k, 4, group);
+    lq_status st = check_group(fn, k, bits, group);
     if (st != LQ_OK) return st;
     if (n > kMaxDim || m > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
     // kernels address a few rows of codes with 32-bit buffer offsets
@@ -112,7 +113,8 @@ lq_status check_w4(const char *fn, const void *x, int64_t m, const void *codes, 
     if (st != LQ_OK) return st;
     const int64_t meta = n * (k / group) * 4;
     if (any_overlap({{y, m * n * 4}},
-                    {{x, m * k * 2}, {codes, n * k / 2}, {scales, meta}, {zeros, symmetric ? 0 : meta}}))
+                    {{x, m * k * 2}, {codes, bits == 4 ? n * k / 2 : n * k}, {scales, meta},
+                     {zeros, symmetric ? 0 : meta}}))
         return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
     return LQ_OK;
 }
@@ -186,23 +188,35 @@ lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const flo
                      int64_t n, int64_t k, int symmetric, int64_t group, float *y, void *stream) {
     const char *fn = "w4a16_gemv";
     if (b > 16) return fail(LQ_ERR_UNSUPPORTED, "%s: batch %lld > 16 (use w4a16_gemm)", fn, (long long)b);
-    lq_status st = check_w4(fn, x_bf16, b, codes, scales, zeros, n, k, symmetric, group, y);
+    lq_status st = check_wo(fn, 4, x_bf16, b, codes, scales, zeros, n, k, symmetric, group, y);
     if (st != LQ_OK || b == 0 || n == 0) return st;
     if ((st = need_device()) != LQ_OK) return st;
-    lq::W4Args a{static_cast<const uint16_t *>(x_bf16), b, static_cast<const uint8_t *>(codes), scales, zeros,
+    lq::WoArgs a{static_cast<const uint16_t *>(x_bf16), b, static_cast<const uint8_t *>(codes), scales, zeros,
                  n, k, symmetric, group, y};
     return launched(lq::launch_w4a16_gemv(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+lq_status w8a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales, const float *zeros,
+                     int64_t n, int64_t k, int symmetric, int64_t group, float *y, void *stream) {
+    const char *fn = "w8a16_gemv";
+    if (b > 16) return fail(LQ_ERR_UNSUPPORTED, "%s: batch %lld > 16", fn, (long long)b);
+    lq_status st = check_wo(fn, 8, x_bf16, b, codes, scales, zeros, n, k, symmetric, group, y);
+    if (st != LQ_OK || b == 0 || n == 0) return st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::WoArgs a{static_cast<const uint16_t *>(x_bf16), b, static_cast<const uint8_t *>(codes), scales, zeros,
+                 n, k, symmetric, group, y};
+    return launched(lq::launch_w8a16_gemv(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 lq_status w4a16_gemm(const void *x_bf16, int64_t m, const void *codes, const float *scales, const float *zeros,
                      int64_t n, int64_t k, int symmetric, int64_t group, float *y, void *stream) {
     const char *fn = "w4a16_gemm";
-    lq_status st = check_w4(fn, x_bf16, m, codes, scales, zeros, n, k, symmetric, group, y);
+    lq_status st = check_wo(fn, 4, x_bf16, m, codes, scales, zeros, n, k, symmetric, group, y);
     if (st != LQ_OK || m == 0 || n == 0) return st;
     // a 128-row activation tile is addressed with 32-bit buffer offsets
     if (k >= (int64_t(1) << 24)) return fail(LQ_ERR_UNSUPPORTED, "%s: k >= 2^24", fn);
     if ((st = need_device()) != LQ_OK) return st;
-    lq::W4Args a{static_cast<const uint16_t *>(x_bf16), m, static_cast<const uint8_t *>(codes), scales, zeros,
+    lq::WoArgs a{static_cast<const uint16_t *>(x_bf16), m, static_cast<const uint8_t *>(codes), scales, zeros,
                  n, k, symmetric, group, y};
     return launched(lq::launch_w4a16_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }

@@ -110,4 +110,44 @@ LQ_DEVICE float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// Transposed exchange across lane halves of width 32 (or 16): afterwards the
+// lanes of the lower half hold a + (partner's a), those of the upper half
+// b + (partner's b). v_permlane{32,16}_swap trades the upper half of its
+// first operand for the lower half of its second.
+LQ_DEVICE float swap_add32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+LQ_DEVICE float swap_add16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum RW (4 or 8) values per lane over the 64 lanes of a wave. Each halving
+// step sends half of the remaining values to the partner lane (lane bits 5,
+// 4, then 3), plain butterflies finish the rest. Afterwards every lane l
+// holds the total of row l >> (6 - log2 RW).
+template <int RW>
+LQ_DEVICE float reduce_rows(float *v, int lane) {
+    static_assert(RW == 4 || RW == 8, "RW must be 4 or 8");
+#pragma unroll
+    for (int i = 0; i < RW / 2; ++i) v[i] = swap_add32(v[i], v[i + RW / 2]);
+#pragma unroll
+    for (int i = 0; i < RW / 4; ++i) v[i] = swap_add16(v[i], v[i + RW / 4]);
+    float t = v[0];
+    if (RW == 8) {
+        // partner lane l ^ 15 sits across bit 3: lanes with bit 3 clear keep row 0 of the pair
+        const bool upper = (lane & 8) != 0;
+        const float keep = upper ? v[1] : v[0];
+        const float send = upper ? v[0] : v[1];
+        t = keep + dpp_move<kDppMirror>(send);
+    } else {
+        t += dpp_move<kDppMirror>(t);
+    }
+    t += dpp_move<kDppHalfMirror>(t);
+    t += dpp_move<kDppXor2>(t);
+    t += dpp_move<kDppXor1>(t);
+    return t;
+}
+
 }  // namespace lq

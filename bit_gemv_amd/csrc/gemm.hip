@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
 
 }  // namespace
 
-hipError_t launch_w4a16_gemm(const W4Args &a, hipStream_t st) {
+hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st) {
     const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
     if (a.symmetric)
         hipLaunchKernelGGL(gemm_w4_kernel<true>, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k,

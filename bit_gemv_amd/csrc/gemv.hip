@@ -61,46 +61,6 @@ LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) 
     return acc;
 }
 
-// Transposed exchange across lane halves of width 32 (or 16): afterwards the
-// lanes of the lower half hold a + (partner's a), those of the upper half
-// b + (partner's b). v_permlane{32,16}_swap trades the upper half of its
-// first operand for the lower half of its second.
-LQ_DEVICE float swap_add32(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-LQ_DEVICE float swap_add16(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Sum RW (4 or 8) values per lane over the 64 lanes of a wave. Each halving
-// step sends half of the remaining values to the partner lane (lane bits 5,
-// 4, then 3), plain butterflies finish the rest. Afterwards every lane l
-// holds the total of row l >> (6 - log2 RW).
-template <int RW>
-LQ_DEVICE float reduce_rows(float *v, int lane) {
-    static_assert(RW == 4 || RW == 8, "RW must be 4 or 8");
-#pragma unroll
-    for (int i = 0; i < RW / 2; ++i) v[i] = swap_add32(v[i], v[i + RW / 2]);
-#pragma unroll
-    for (int i = 0; i < RW / 4; ++i) v[i] = swap_add16(v[i], v[i + RW / 4]);
-    float t = v[0];
-    if (RW == 8) {
-        // partner lane l ^ 15 sits across bit 3: lanes with bit 3 clear keep row 0 of the pair
-        const bool upper = (lane & 8) != 0;
-        const float keep = upper ? v[1] : v[0];
-        const float send = upper ? v[0] : v[1];
-        t = keep + dpp_move<kDppMirror>(send);
-    } else {
-        t += dpp_move<kDppMirror>(t);
-    }
-    t += dpp_move<kDppHalfMirror>(t);
-    t += dpp_move<kDppXor2>(t);
-    t += dpp_move<kDppXor1>(t);
-    return t;
-}
-
 // ---------------------------------------------------------------------------
 // VALU kernel, batch B <= 4.
 // Block = 4 waves. The waves split the 2048-wide chunks of k (ks_count ways)
@@ -605,7 +565,7 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
 }
 
 template <int B, int RW, bool SYM>
-static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st, int ks_count) {
+static hipError_t launch_valu_rw(const WoArgs &a, hipStream_t st, int ks_count) {
     // staged scales need whole 4-group runs per row: k a multiple of 512
     const bool g128 = a.group == 128 && a.k % 512 == 0;
     const int rows_per_block = (4 / ks_count) * RW;
@@ -624,7 +584,7 @@ static hipError_t launch_valu_rw(const W4Args &a, hipStream_t st, int ks_count) 
 // (then each wave walks several chunks), not at all for one chunk; a wave
 // takes 8 rows unless that leaves fewer than 512 blocks to fill the chip.
 template <int B, bool SYM>
-static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
+static hipError_t launch_valu(const WoArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
     const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
     const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
@@ -634,7 +594,7 @@ static hipError_t launch_valu(const W4Args &a, hipStream_t st) {
 // Waves per block: enough to put about 2048 waves on the chip (8 per CU),
 // 4 to 16, and no more than there are groups; then the runs are balanced.
 template <bool SYM>
-static hipError_t launch_mfma(const W4Args &a, hipStream_t st) {
+static hipError_t launch_mfma(const WoArgs &a, hipStream_t st) {
     const int64_t blocks = (a.n + kMfmaRows - 1) / kMfmaRows;
     const int ng128 = (int)(a.k / 128);
     int wpb = 4;
@@ -652,7 +612,7 @@ static hipError_t launch_mfma(const W4Args &a, hipStream_t st) {
 // (batch x k x 2 bytes) fits 32 bits; the register-streaming MFMA kernel
 // for taller matrices.
 template <bool SYM>
-static hipError_t launch_batch(const W4Args &a, hipStream_t st) {
+static hipError_t launch_batch(const WoArgs &a, hipStream_t st) {
     if (a.n <= 12288 && a.m * a.k * 2 < (int64_t(1) << 32)) {
         if (a.m <= 8)
             hipLaunchKernelGGL((gemv_ring_kernel<8, SYM>), dim3((uint32_t)((a.n + 15) / 16)), dim3(256), 0, st, a.x,
@@ -666,7 +626,7 @@ static hipError_t launch_batch(const W4Args &a, hipStream_t st) {
 }
 
 template <bool SYM>
-static hipError_t launch_gemv_s(const W4Args &a, hipStream_t st) {
+static hipError_t launch_gemv_s(const WoArgs &a, hipStream_t st) {
     switch (a.m) {
         case 1: return launch_valu<1, SYM>(a, st);
         case 2: return launch_valu<2, SYM>(a, st);
@@ -676,7 +636,7 @@ static hipError_t launch_gemv_s(const W4Args &a, hipStream_t st) {
     }
 }
 
-hipError_t launch_w4a16_gemv(const W4Args &a, hipStream_t st) {
+hipError_t launch_w4a16_gemv(const WoArgs &a, hipStream_t st) {
     if (a.m < 1 || a.m > 16) return hipErrorInvalidValue;
     return a.symmetric ? launch_gemv_s<true>(a, st) : launch_gemv_s<false>(a, st);
 }

@@ -25,7 +25,8 @@ struct DequantArgs {
     float *out;
 };
 
-struct W4Args {
+// Weight-only products (W4A16 and W8A16): bf16 activations, integer codes.
+struct WoArgs {
     const uint16_t *x;
     int64_t m;  // batch (GEMV) or tokens (GEMM)
     const uint8_t *codes;
@@ -66,8 +67,9 @@ struct W8Args {
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
-hipError_t launch_w4a16_gemv(const W4Args &a, hipStream_t st);
-hipError_t launch_w4a16_gemm(const W4Args &a, hipStream_t st);
+hipError_t launch_w4a16_gemv(const WoArgs &a, hipStream_t st);
+hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st);
+hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st);
 hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st);
 hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st);
 hipError_t launch_w8a8_gemm(const W8Args &a, hipStream_t st);

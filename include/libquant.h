@@ -143,6 +143,25 @@ lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const flo
                      float *y, void *stream);
 
 /*
+ * w8a16_gemv -- batch-b decode product with INT8 weights
+ * ("LLM quantization deep dive", W/A/KV notation: W8A16 keeps 8-bit weights
+ * and 16-bit activations; as for W4A16 the codes are dequantized inside the
+ * kernel and multiplied with the activations, higher-precision
+ * accumulation):
+ *   y[i][r] = sum_j x[i][j] * (q[r][j] - z[r][j/group]) * s[r][j/group]
+ * x_bf16  [b][k] bf16 activations, b in 0..16 (larger: LQ_ERR_UNSUPPORTED).
+ * codes   [n][k] INT8 codes from quantize_groupwise(bits = 8): int8 q for
+ *         symmetric, uint8 q for asymmetric.
+ * scales  fp32 [n][k/group]; zeros fp32 [n][k/group] or NULL if symmetric.
+ * y       out fp32 [b][n].
+ * group: multiple of 128 dividing k; k multiple of 128 and at most 2^28.
+ * Errors as w4a16_gemv; x, codes and y must be 16-byte aligned.
+ */
+lq_status w8a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales,
+                     const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,
+                     float *y, void *stream);
+
+/*
  * w4a16_gemm -- prefill-shaped product with INT4 weights, same definition
  * as w4a16_gemv for any m ("LLM quantization deep dive", prefill is
  * compute-bound; "3.6 Quantization", W4A16 does not speed up prefill).

@@ -90,6 +90,7 @@ def test_quantize_rejects(lib, kwargs, status):
 def test_empty_work_is_ok(lib):
     assert _q(lib, w=None, n=0, codes=None, scales=None, zeros=None) == 0
     assert lib.w4a16_gemv(None, 0, None, None, None, 8, 256, 1, 128, None, None) == 0
+    assert lib.w8a16_gemv(None, 0, None, None, None, 8, 256, 1, 128, None, None) == 0
     assert lib.w4a16_gemm(None, 5, None, None, None, 0, 256, 1, 128, None, None) == 0
     assert lib.quant_per_token_int8(None, 0, 256, None, None, None, None) == 0
     assert lib.w8a8_gemm(None, None, 0, None, None, 4, 256, None, None, None) == 0
@@ -104,8 +105,22 @@ def test_empty_work_is_ok(lib):
     ((A16, 1, B16, C16, None, 8, 200, 1, 100, D16), 2),       # group not a multiple of 128
     ((A16, 1, B16, C16, None, 8, 256, 1, 128, A16), 1),       # y aliases x
 ])
-def test_gemv_rejects(lib, args, status):
-    assert lib.w4a16_gemv(*args, None) == status
+@pytest.mark.parametrize("fn", ["w4a16_gemv", "w8a16_gemv"])
+def test_gemv_rejects(lib, fn, args, status):
+    assert getattr(lib, fn)(*args, None) == status
+
+
+def test_w8a16_gemv_checks_overlap_with_one_byte_codes(lib):
+    """INT8 codes take n * k bytes: an output starting half-way through them
+    overlaps (it would not for INT4's n * k / 2)."""
+    n, k = 8, 256
+    codes = 2 << 20
+    y = P(codes + n * k // 2 + 16)
+    x, scales = P(1 << 20), P(3 << 20)
+    assert lib.w8a16_gemv(x, 1, P(codes), scales, None, n, k, 1, 128, y, None) == 1
+    assert b"overlap" in lib.lq_last_error()
+    if torch.cuda.device_count() == 0:
+        assert lib.w4a16_gemv(x, 1, P(codes), scales, None, n, k, 1, 128, y, None) == 4
 
 
 def test_gemm_rejects_k_beyond_32bit_tile_offsets(lib):

@@ -1,0 +1,108 @@
+"""W8A16 GEMV (batch 1..16) against the oracle's fp64 result on the same INT8 codes."""
+import numpy as np
+import pytest
+
+import bit_gemv_amd as bg
+import oracle
+from gpu_helpers import assert_close, assert_same_bits, dev_bf16, host, say
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(n, k, b, sym, group=128, seed=0, w_scale=0.02, x_mult=None):
+    rng = np.random.default_rng(seed)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * w_scale)
+    xf = rng.standard_normal((b, k))
+    if x_mult is not None:
+        xf = xf * x_mult
+    x = f32_to_bf16_bits(xf)
+    say(f"w8a16 gemv n={n} k={k} b={b} sym={sym} group={group}")
+    pw = bg.quantize_groupwise(dev_bf16(w), 8, sym, group)
+    c_ref, s_ref, z_ref = oracle.quantize(w, 8, sym, group)
+    assert_same_bits(host(pw.codes), c_ref, "codes")
+    y = host(bg.w8a16_gemv(dev_bf16(x), pw))
+    y_ref = oracle.w8a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, group)
+    assert_close(y, y_ref, f"y n={n} k={k} b={b}")
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(1, 128), (5, 384), (67, 2048 + 128), (300, 4096), (129, 11008),
+                                 (96, 8192), (33, 28672)])
+def test_batch1_shapes(n, k, sym):
+    """One to many chunks of 1024 k, a half-filled last chunk, ragged rows."""
+    _case(n, k, 1, sym)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(16384 + 37, 2048 + 512), (20000, 8192), (8192 + 3, 16384 + 512),
+                                 (4096 + 5, 4096 + 128)])
+def test_tall_batch1(n, k, sym):
+    """Tall matrices (8 rows per wave) with ragged rows and partial chunks."""
+    _case(n, k, 1, sym, seed=n % 97)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 7, 8, 9, 12, 16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_batches(b, sym):
+    """Every kernel batch width (1..4 exact, 8 and 16 with unused rows)."""
+    _case(203, 4096 + 640, b, sym, seed=b)
+
+
+@pytest.mark.parametrize("b", [1, 4, 8, 16])
+def test_batches_tall(b):
+    _case(12288 + 7, 4096, b, False, seed=b + 40)
+
+
+@pytest.mark.parametrize("b", [1, 6])
+@pytest.mark.parametrize("group,k", [(256, 4096), (384, 1152 * 3), (1024, 4096), ("k", 3072), ("k", 128)])
+def test_larger_groups(b, group, k):
+    """Groups wider than 128, one not dividing the 1024-wide chunk (384), and
+    per-channel (one group per row)."""
+    _case(300, k, b, False, group=k if group == "k" else group, seed=b)
+
+
+def test_activation_outlier_channels():
+    k = 4096
+    mult = np.ones(k)
+    mult[[5, 900, 4000]] = [20.0, 40.0, 60.0]
+    _case(128, k, 4, True, x_mult=mult, seed=3)
+
+
+def test_extreme_codes():
+    """Weights whose groups hit every end code: q = -127 / 127 (symmetric) and
+    0 / 255 (asymmetric), the bytes where the unsigned conversion and the
+    0x80 flip matter most."""
+    rng = np.random.default_rng(7)
+    n, k = 64, 2048
+    w = rng.standard_normal((n, k)) * 0.02
+    w[:, ::128] = 0.5
+    w[:, 1::128] = -0.5
+    wb = f32_to_bf16_bits(w)
+    x = f32_to_bf16_bits(rng.standard_normal((3, k)))
+    for sym in (False, True):
+        say(f"w8a16 extreme codes sym={sym}")
+        pw = bg.quantize_groupwise(dev_bf16(wb), 8, sym, 128)
+        c_ref, s_ref, z_ref = oracle.quantize(wb, 8, sym, 128)
+        assert_same_bits(host(pw.codes), c_ref, "codes")
+        y = host(bg.w8a16_gemv(dev_bf16(x), pw))
+        assert_close(y, oracle.w8a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, 128), f"extreme sym={sym}")
+
+
+def test_int4_codes_are_refused():
+    import torch
+    w = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    pw = bg.quantize_groupwise(w, 4, True, 128)
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        bg.w8a16_gemv(x, pw)
+
+
+def test_batch_over_16_is_unsupported():
+    import torch
+    w = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    pw = bg.quantize_groupwise(w, 8, True, 128)
+    x = torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bg.LibquantError) as e:
+        bg.w8a16_gemv(x, pw)
+    assert e.value.status == bg.LQ_ERR_UNSUPPORTED
