@@ -276,7 +276,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
         lines.append(f"| `{short}` | {gx} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e6:.3f} |")
     # the fused gate|up launch: 57344 rows / 8 rows per block -> 7168 blocks x 256 work-items
     for name, cnt, avg, mn, mx, tot, gx in rows:
-        if "gemv_valu_kernel<1, 8, false>" in name and gx == 7168 * 256:
+        if "gemv_valu_kernel<1, 8, false, true>" in name and gx == 7168 * 256:
             dom_avg = avg / 1e3
     lines += ["", f"Fused gate|up batch-1 GEMV (57344 x 8192, grid {7168 * 256}): average "
                   f"{dom_avg:.2f} us per launch." if dom_avg else ""]
@@ -303,7 +303,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
     n, k = 57344, 8192
     alg = w4_bytes(n, k, 1, wl.symmetric, wl.group)
     hbm = f_kib * 1024 / ffac + w_kib * 1024 / wfac
-    out = {"kernel": "lq::gemv_valu_kernel<1, 8, false> (w4a16_gemv, batch 1, asymmetric)",
+    out = {"kernel": "lq::gemv_valu_kernel<1, 8, false, true> (w4a16_gemv, batch 1, asymmetric, staged scales)",
            "workload": "llama70b_decode fused gate|up", "n": n, "k": k,
            "kernel_source_sha256_16": kernel_source_hash(),
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
