@@ -25,6 +25,11 @@ hold the pins):
   matmul of the codes, the exactness of the smoothing identity and the toy
   error ratio of the code block.
 * ``effective_bits`` / ``packed_bytes``: the printed effective-bit values.
+* ``act_absmean`` / ``awq_scale`` / ``awq_loss`` / ``awq_search``: numpy
+  recomputations of the channel means and of the output error from the
+  pinned quantizer, the reduction to plain RTN at alpha = 0, and the pages'
+  claims (scaling a channel by s shrinks its rounding error about 1/s; the
+  search beats plain RTN when activations have outlier channels).
 """
 from __future__ import annotations
 
@@ -74,6 +79,11 @@ def _load():
         lib.oracle_dequantize.argtypes = [P, P, P, I64, I64, I, I, I64, P]
         lib.oracle_w4a16_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I64, P]
         lib.oracle_weight_only_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I, I64, P]
+        lib.oracle_act_absmean.argtypes = [P, I64, I64, P]
+        lib.oracle_awq_scale.argtypes = [P, I64, I, I, P]
+        lib.oracle_awq_scale.restype = None
+        lib.oracle_awq_loss.argtypes = [P, I64, P, I64, I64, I, I, I64, P, P]
+        lib.oracle_awq_search.argtypes = [P, I64, P, I64, I64, I, I, I64, I, P, P, P, P]
         lib.oracle_smooth_scale_from_absmax.argtypes = [P, P, I64, F, P]
         lib.oracle_smooth_scale_from_absmax.restype = None
         lib.oracle_smooth_scale.argtypes = [P, I64, P, I64, I64, F, P]
@@ -228,3 +238,51 @@ def packed_bytes(n: int, k: int, bits: int, symmetric: bool, group: int) -> int:
 def bf16_bits_to_f32(h) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (for the tests' own checks)."""
     return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def act_absmean(x_bf16):
+    """s_X[k] = mean_t |X[t][k]| (fp64 sum, one fp32 rounding); x: bf16 bits [t][k]."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    t, k = x.shape
+    sx = np.zeros(k, np.float32)
+    _check(lib.oracle_act_absmean(_ptr(x), t, k, _ptr(sx)), "act_absmean")
+    return sx
+
+
+def awq_scale(sx, i: int, n_grid: int):
+    """Grid point i's scale: powf(max(s_X, 1e-8), i / n_grid)."""
+    lib = _load()
+    sx = _c(sx, np.float32)
+    s = np.zeros(sx.size, np.float32)
+    lib.oracle_awq_scale(_ptr(sx), sx.size, int(i), int(n_grid), _ptr(s))
+    return s
+
+
+def awq_loss(x_bf16, w_bf16, s, bits: int, symmetric: bool, group: int) -> float:
+    """|| X W^T - bf16(X / s) quant(W diag(s))^T ||_F^2 in fp64."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    t, k = x.shape
+    n = w.shape[0]
+    out = np.zeros(1, np.float64)
+    _check(lib.oracle_awq_loss(_ptr(x), t, _ptr(w), n, k, bits, int(bool(symmetric)), group,
+                               _ptr(_c(s, np.float32)), _ptr(out)), "awq_loss")
+    return float(out[0])
+
+
+def awq_search(x_bf16, w_bf16, bits: int, symmetric: bool, group: int, n_grid: int):
+    """AWQ grid search -> (s_X [k], losses [n_grid + 1], best index, s_best [k])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    t, k = x.shape
+    n = w.shape[0]
+    sx = np.zeros(k, np.float32)
+    losses = np.zeros(n_grid + 1, np.float64)
+    best = np.zeros(1, np.int32)
+    s_best = np.zeros(k, np.float32)
+    _check(lib.oracle_awq_search(_ptr(x), t, _ptr(w), n, k, bits, int(bool(symmetric)), group, int(n_grid),
+                                 _ptr(sx), _ptr(losses), _ptr(best), _ptr(s_best)), "awq_search")
+    return sx, losses, int(best[0]), s_best

@@ -412,3 +412,147 @@ int64_t oracle_packed_bytes(int64_t n, int64_t k, int bits, int symmetric, int64
     const int64_t meta = n * (k / group) * 4 * (symmetric ? 1 : 2);
     return codes + meta;
 }
+
+/* ------------------------------------------------------------------------
+ * AWQ activation-aware scaling ([LP] "AWQ: protecting salient channels by
+ * scaling"; [CP] AWQ, steps 1-5; [RL] section 5, activation-aware).
+ *
+ * A weight input channel j that multiplies large activations is protected
+ * by scaling it up before RTN and the activation down by the same factor:
+ *   y = sum_j (s_j w_j)(x_j / s_j)  ->  sum_j quant(s_j w_j) x_j / s_j.
+ * [LP]: s = s_X^alpha with s_X the mean activation magnitude of each input
+ * channel over the calibration data, alpha chosen per layer by a grid
+ * search over [0, 1] that minimises the layer's output error on that data;
+ * 1/s is folded into the preceding operation.
+ * Readings (the pages leave these open):
+ *  - the grid is alpha_i = i / n_grid, i = 0 .. n_grid (both ends of [0, 1]);
+ *  - s_X is floored at 1e-8 (the pages' only floor constant) before the
+ *    power, so a silent channel gives a finite scale;
+ *  - the scaled weights are quantized group-wise exactly as quantize_groupwise
+ *    does with col_scale = s (fp32 product, not re-rounded);
+ *  - the activations reach the quantized product as bf16(x / s): the
+ *    preceding operation, with 1/s folded in, emits bf16;
+ *  - output error = squared Frobenius norm of X W^T - X' W_hat'^T over the
+ *    calibration tokens, in fp64 (X W^T from the bf16 inputs, exact products);
+ *  - ties between grid points keep the smallest alpha.
+ * ---------------------------------------------------------------------- */
+
+/* fp32 -> bf16 bits, round to nearest even (finite inputs). */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* s_X[j] = (sum_t |X[t][j]|) / t: the sum in fp64 in token order, divided in
+ * fp64 and rounded once to fp32. x: bf16 bits [t][k]. */
+int oracle_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx)
+{
+    if (t <= 0 || k <= 0) return -1;
+    for (int64_t j = 0; j < k; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < t; ++i) acc += fabs((double)bf16_bits_to_f32(x[i * k + j]));
+        sx[j] = (float)(acc / (double)t);
+    }
+    return 0;
+}
+
+/* The candidate scale of grid point i: powf(max(s_X, 1e-8), i / n_grid). */
+void oracle_awq_scale(const float *sx, int64_t k, int i, int n_grid, float *s)
+{
+    const float alpha = (float)i / (float)n_grid;
+    for (int64_t j = 0; j < k; ++j) {
+        const float v = sx[j] < ORACLE_FLOOR ? ORACLE_FLOOR : sx[j];
+        s[j] = powf(v, alpha);
+    }
+}
+
+/* Output error of one scale vector s [k] against y_ref = X W^T [t][n]. */
+static int awq_loss_given_ref(const uint16_t *x, int64_t t, const uint16_t *w, int64_t n, int64_t k,
+                              int bits, int symmetric, int64_t group, const float *s,
+                              const double *y_ref, double *loss)
+{
+    const int64_t ng = k / group;
+    const int64_t code_bytes = bits == 4 ? n * k / 2 : n * k;
+    uint8_t *codes = (uint8_t *)malloc((size_t)code_bytes);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)(n * ng));
+    float *zr = (float *)malloc(sizeof(float) * (size_t)(n * ng));
+    float *w_hat = (float *)malloc(sizeof(float) * (size_t)(n * k));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)(t * k));
+    int rc = -1;
+    if (!codes || !sc || !zr || !w_hat || !xs) goto out;
+    /* W' = quant(W diag(s)), dequantized */
+    if (oracle_quantize_bf16(w, n, k, bits, symmetric, group, s, codes, sc, zr)) goto out;
+    if (oracle_dequantize(codes, sc, symmetric ? NULL : zr, n, k, bits, symmetric, group, w_hat)) goto out;
+    /* X' = bf16(X / s) */
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t j = 0; j < k; ++j)
+            xs[i * k + j] = bf16_bits_to_f32(f32_to_bf16_rne(bf16_bits_to_f32(x[i * k + j]) / s[j]));
+    double total = 0.0;
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t r = 0; r < n; ++r) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j) acc += (double)xs[i * k + j] * (double)w_hat[r * k + j];
+            const double d = y_ref[i * n + r] - acc;
+            total += d * d;
+        }
+    *loss = total;
+    rc = 0;
+out:
+    free(codes); free(sc); free(zr); free(w_hat); free(xs);
+    return rc;
+}
+
+static double *awq_reference_output(const uint16_t *x, int64_t t, const uint16_t *w, int64_t n, int64_t k)
+{
+    double *y = (double *)malloc(sizeof(double) * (size_t)(t * n));
+    if (!y) return NULL;
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t r = 0; r < n; ++r) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)bf16_bits_to_f32(w[r * k + j]);
+            y[i * n + r] = acc;
+        }
+    return y;
+}
+
+/* Output error of a given scale vector s [k] (one grid point, or any s). */
+int oracle_awq_loss(const uint16_t *x, int64_t t, const uint16_t *w, int64_t n, int64_t k, int bits,
+                    int symmetric, int64_t group, const float *s, double *loss)
+{
+    if (check_args(n, k, bits, group) || t <= 0) return -1;
+    double *y_ref = awq_reference_output(x, t, w, n, k);
+    if (!y_ref) return -1;
+    const int rc = awq_loss_given_ref(x, t, w, n, k, bits, symmetric, group, s, y_ref, loss);
+    free(y_ref);
+    return rc;
+}
+
+/* The search: s_X, the loss of every grid point (losses [n_grid + 1]), the
+ * first grid point with the smallest loss (best) and its scale (s_best [k]). */
+int oracle_awq_search(const uint16_t *x, int64_t t, const uint16_t *w, int64_t n, int64_t k, int bits,
+                      int symmetric, int64_t group, int n_grid, float *sx, double *losses, int *best,
+                      float *s_best)
+{
+    if (check_args(n, k, bits, group) || t <= 0 || n <= 0 || n_grid < 1) return -1;
+    if (oracle_act_absmean(x, t, k, sx)) return -1;
+    double *y_ref = awq_reference_output(x, t, w, n, k);
+    float *s = (float *)malloc(sizeof(float) * (size_t)k);
+    int rc = -1;
+    if (!y_ref || !s) goto out;
+    int arg = 0;
+    for (int i = 0; i <= n_grid; ++i) {
+        oracle_awq_scale(sx, k, i, n_grid, s);
+        if (awq_loss_given_ref(x, t, w, n, k, bits, symmetric, group, s, y_ref, &losses[i])) goto out;
+        if (losses[i] < losses[arg]) arg = i;
+    }
+    *best = arg;
+    oracle_awq_scale(sx, k, arg, n_grid, s_best);
+    rc = 0;
+out:
+    free(y_ref); free(s);
+    return rc;
+}

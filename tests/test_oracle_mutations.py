@@ -38,6 +38,16 @@ MUTANTS = {
                                "const int64_t codes_per_row = k / 2;"),
     "int8_sym_read_unsigned": ("return symmetric ? (int32_t)(int8_t)row_codes[j] : (int32_t)row_codes[j];",
                                "return (int32_t)row_codes[j];"),
+    "awq_grid_misses_one": ("const float alpha = (float)i / (float)n_grid;",
+                            "const float alpha = (float)i / (float)(n_grid + 1);"),
+    "awq_channel_max_not_mean": ("for (int64_t i = 0; i < t; ++i) acc += fabs((double)bf16_bits_to_f32(x[i * k + j]));",
+                                 "for (int64_t i = 0; i < t; ++i) acc = fmax(acc, (double)t * fabs((double)bf16_bits_to_f32(x[i * k + j])));"),
+    "awq_activation_times_s": ("f32_to_bf16_rne(bf16_bits_to_f32(x[i * k + j]) / s[j])",
+                               "f32_to_bf16_rne(bf16_bits_to_f32(x[i * k + j]) * s[j])"),
+    "awq_weights_unscaled": ("if (oracle_quantize_bf16(w, n, k, bits, symmetric, group, s, codes, sc, zr)) goto out;",
+                             "if (oracle_quantize_bf16(w, n, k, bits, symmetric, group, NULL, codes, sc, zr)) goto out;"),
+    "awq_argmax": ("if (losses[i] < losses[arg]) arg = i;", "if (losses[i] > losses[arg]) arg = i;"),
+    "awq_abs_error": ("total += d * d;", "total += fabs(d);"),
     "smooth_inverted": ("s[j] = sqrtf(a) / sqrtf(b);", "s[j] = sqrtf(b) / sqrtf(a);"),
     "smooth_alpha_swapped": ("s[j] = powf(a, alpha) / powf(b, 1.0f - alpha);",
                              "s[j] = powf(a, 1.0f - alpha) / powf(b, alpha);"),

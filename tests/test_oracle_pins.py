@@ -478,3 +478,106 @@ def test_int32_accumulator_bound_for_largest_k():
 def test_invalid_arguments_rejected():
     with pytest.raises(ValueError):
         oracle.quantize(np.zeros((2, 100), f32), 4, True, 128)
+
+
+# --------------------------------------------------------------------------
+# AWQ activation-aware scaling ("3.6 Quantization", AWQ section).
+# --------------------------------------------------------------------------
+def _bf16_rne_np(a):
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(a, np.float32)))
+
+
+def _awq_case(seed, t=24, n=40, k=384, outliers=(7, 200), mult=30.0):
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    xf = rng.standard_normal((t, k)).astype(f32)
+    xf[:, list(outliers)] *= f32(mult)
+    x = f32_to_bf16_bits(xf)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    return x, w
+
+
+def test_act_absmean_is_the_channel_mean_magnitude():
+    from workloads import bf16_bits_to_f32
+    x, _ = _awq_case(30)
+    sx = oracle.act_absmean(x)
+    ref = np.abs(bf16_bits_to_f32(x).astype(np.float64)).mean(axis=0)
+    assert np.array_equal(sx, ref.astype(f32))
+
+
+def test_awq_scale_grid_ends():
+    """alpha = 0 gives s = 1 (plain RTN); alpha = 1 gives s = s_X; a zero
+    channel is floored at 1e-8 first."""
+    sx = np.array([0.5, 2.0, 0.0, 37.25], f32)
+    assert np.array_equal(oracle.awq_scale(sx, 0, 20), np.ones(4, f32))
+    assert np.array_equal(oracle.awq_scale(sx, 20, 20), np.array([0.5, 2.0, 1e-8, 37.25], f32))
+    half = oracle.awq_scale(sx, 10, 20)
+    assert np.allclose(half, np.sqrt(np.maximum(sx, 1e-8)), rtol=1e-6)
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_awq_loss_recomputed_in_numpy(symmetric):
+    """The loss from its definition: quantize W diag(s) (pinned quantizer),
+    dequantize, X / s rounded to bf16, fp64 products."""
+    from workloads import bf16_bits_to_f32
+    x, w = _awq_case(31)
+    t, k = x.shape
+    n = w.shape[0]
+    rng = np.random.default_rng(5)
+    s = np.exp(rng.uniform(-1.0, 1.5, k)).astype(f32)
+    got = oracle.awq_loss(x, w, s, 4, symmetric, 128)
+    codes, sc, z = oracle.quantize(w, 4, symmetric, 128, col_scale=s)
+    w_hat = oracle.dequantize(codes, sc, z, n, k, 4, symmetric, 128).astype(np.float64)
+    xf = bf16_bits_to_f32(x)
+    xs = _bf16_rne_np(xf / s).astype(np.float64)
+    y_ref = xf.astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
+    ref = float(((y_ref - xs @ w_hat.T) ** 2).sum())
+    assert got == pytest.approx(ref, rel=1e-12)
+
+
+def test_awq_alpha_zero_is_plain_rtn():
+    """At alpha = 0 the search evaluates plain group-wise RTN."""
+    from workloads import bf16_bits_to_f32
+    x, w = _awq_case(32)
+    t, k = x.shape
+    n = w.shape[0]
+    sx, losses, best, s_best = oracle.awq_search(x, w, 4, False, 128, 20)
+    codes, sc, z = oracle.quantize(w, 4, False, 128)
+    w_hat = oracle.dequantize(codes, sc, z, n, k, 4, False, 128).astype(np.float64)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    rtn = float(((xf @ bf16_bits_to_f32(w).astype(np.float64).T - xf @ w_hat.T) ** 2).sum())
+    assert losses[0] == pytest.approx(rtn, rel=1e-12)
+    assert losses.shape == (21,)
+    assert best == int(np.argmin(losses))
+    assert np.array_equal(s_best, oracle.awq_scale(sx, best, 20))
+
+
+def test_awq_search_protects_outlier_channels():
+    """The AWQ section's claim: with a few activation channels far larger
+    than the rest, scaling them before RTN lowers the output error, so the
+    search lands on alpha > 0 and beats plain RTN clearly."""
+    x, w = _awq_case(33, t=32, n=64, k=512, outliers=(3, 77, 300, 411), mult=40.0)
+    _, losses, best, _ = oracle.awq_search(x, w, 4, False, 128, 20)
+    assert best > 0
+    assert losses[best] < 0.8 * losses[0]
+
+
+def test_awq_scaling_shrinks_a_channels_error_about_1_over_s():
+    """The AWQ section: multiplying one weight channel by s leaves the group
+    range (set by the other weights) unchanged, so its rounding error after
+    dividing by s falls by about 1/s. Over many groups, channel 5 scaled by
+    4 has a mean absolute error near a quarter of the unscaled one."""
+    rng = np.random.default_rng(34)
+    n, k = 2000, 128
+    w = rng.uniform(-1.0, 1.0, (n, k)).astype(f32)
+    w[:, 0], w[:, 1] = 1.0, -1.0          # every group's range is [-1, 1]
+    w[:, 5] *= f32(0.2)                   # scaled by 4 it stays inside the range
+    s = np.ones(k, f32)
+    s[5] = 4.0
+    def err(cs):
+        codes, sc, z = oracle.quantize(w, 4, False, 128, col_scale=cs)
+        w_hat = oracle.dequantize(codes, sc, z, n, k, 4, False, 128)
+        return np.abs(w_hat[:, 5] / cs[5] - w[:, 5]).mean()
+    e1, e4 = err(np.ones(k, f32)), err(s)
+    assert 0.18 < e4 / e1 < 0.32

@@ -190,5 +190,13 @@ WORKLOADS = {
         symmetric=True, group=8192, batches=(512,), x_outlier_count=6,
         x_outlier_mults=(50.0,) * 6, tokens=512, extra={"alpha": 0.5},
         notes="SmoothQuant W8A8: X 512x8192 with 6 channels x50, W 8192x8192, alpha 0.5"),
+    # AWQ's per-layer scale search: calibration activations with fixed outlier
+    # channels (the salient channels the method protects) against the
+    # Llama-2-7B layer shapes, asymmetric INT4 G = 128, alpha on a 21-point grid
+    "awq7b": Workload(
+        index=5, name="awq7b", linears=LLAMA7B, layers=1, bits=4, symmetric=False, group=128,
+        batches=(512,), x_outlier_count=41, x_outlier_mults=(20.0,) * 41, tokens=512,
+        extra={"n_grid": 20},
+        notes="AWQ scale search: X 512 tokens with 41 channels x20, Llama-2-7B layer, asymmetric INT4 G=128"),
 }
 WORKLOAD_ORDER = ["single_4096", "llama7b_decode", "llama70b_decode", "prefill70b", "smoothquant"]
