@@ -98,7 +98,7 @@ def _timed(fn, reps: int = 5) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def measure_rows(dev, packed, shapes, names, wl) -> dict:
+def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
     """Live measurement of every other step of the path on its own workload."""
     import numpy as np
     import torch
@@ -110,10 +110,29 @@ def measure_rows(dev, packed, shapes, names, wl) -> dict:
         return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).to(dev)
 
     rows = {}
+    # a6 at batch 4 and 16: the same W4A16 stack, a whole token per replay
+    w4b = {}
+    sym, group = wl.symmetric, wl.group
+    for b in (4, 16):
+        xs = {k: dev_bf16(wl.activation(k, b)) for k in sorted({k for _, k in shapes})}
+        ys = [torch.empty((b, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+
+        def sweep4():
+            for layer in range(wl.layers):
+                for j, (n, k) in enumerate(shapes):
+                    bg.w4a16_gemv(xs[k], packed[layer][j], ys[j])
+
+        ms = _graph_ms(sweep4, reps=5)
+        byt = wl.layers * sum(w4_bytes(n, k, b, sym, group) for n, k in shapes)
+        tbs = byt / (ms * 1e-3) / 1e12
+        w4b[f"batch{b}"] = {"ms_per_token_step": round(ms, 4), "TBps": round(tbs, 4),
+                            "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4), "bytes": byt}
+        log(f"[bench] w4a16_gemv {wl.name} batch {b}: {ms:.3f} ms/step, {tbs:.3f} TB/s")
+        del xs, ys
+    rows["w4a16_gemv_decode_batches"] = {"workload": wl.name, "layers": wl.layers, "bound": "hbm", **w4b}
+
     # f3: W8A16 decode, the same layers with INT8 codes, a whole token (every
     # layer, address-distinct buffers) per graph replay at batch 1, 4 and 16
-    groups = [[0, 1, 2], [3], [4, 5], [6]] if len(wl.linears) == 7 else [[i] for i in range(len(wl.linears))]
-    sym, group = wl.symmetric, wl.group
     n_sets = min(wl.distinct_layers, 2)
     src = []
     for s_ in range(n_sets):
@@ -576,7 +595,7 @@ def main() -> int:
         result["rows"] = {"quantize_pack": {"workload": wl.name, "weights": q_elems, "ms": round(q_ms, 3),
                                             "GBps": round(quant_gbs, 1), "bound": "hbm",
                                             "frac_of_peak": round(quant_gbs / HBM_PEAK_GBS, 4)}}
-        result["rows"].update(measure_rows(dev, packed, shapes, names, wl))
+        result["rows"].update(measure_rows(dev, packed, shapes, names, wl, groups))
 
     del packed
     torch.cuda.empty_cache()
