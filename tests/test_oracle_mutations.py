@@ -32,8 +32,8 @@ MUTANTS = {
     "dequant_plus_z": ("out[r * k + j] = (qf - z) * s;", "out[r * k + j] = (qf + z) * s;"),
     "matmul_transposed_x": ("acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];",
                             "acc += (double)bf16_bits_to_f32(x[j * m + i < m * k ? j * m + i : 0]) * (double)wrow[j];"),
-    "matmul_drops_last_element": ("for (int64_t j = 0; j < k; ++j)\n                acc +=",
-                                  "for (int64_t j = 0; j + 1 < k; ++j)\n                acc +="),
+    "matmul_drops_last_element": ("for (int64_t j = 0; j < k; ++j)\n                acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];",
+                                  "for (int64_t j = 0; j + 1 < k; ++j)\n                acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];"),
     "int8_row_stride_halved": ("const int64_t codes_per_row = bits == 4 ? k / 2 : k;",
                                "const int64_t codes_per_row = k / 2;"),
     "int8_sym_read_unsigned": ("return symmetric ? (int32_t)(int8_t)row_codes[j] : (int32_t)row_codes[j];",
