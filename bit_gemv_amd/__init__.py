@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libquant.so")
 LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = range(5)
 
 ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w8a16_gemv", "w4a16_gemm",
-                "smooth_scale", "quant_per_token_int8", "w8a8_gemm")
+                "smooth_scale", "quant_per_token_int8", "w8a8_gemm", "act_absmean", "awq_search")
 
 
 class LibquantError(RuntimeError):
@@ -58,6 +58,8 @@ def load_library(path: Optional[str] = None):
         "smooth_scale": [P, I64, P, I64, I64, F, P, P],
         "quant_per_token_int8": [P, I64, I64, P, P, P, P],
         "w8a8_gemm": [P, P, I64, P, P, I64, I64, P, P, P],
+        "act_absmean": [P, I64, I64, P, P],
+        "awq_search": [P, I64, P, I64, I64, I, I64, I, P, P, I64, P, P, P, P, P, P, P],
     }
     for name, argtypes in sigs.items():
         fn = getattr(lib, name)
@@ -68,6 +70,8 @@ def load_library(path: Optional[str] = None):
     lib.lq_status_string.restype = ctypes.c_char_p
     lib.lq_status_string.argtypes = [ctypes.c_int]
     lib.lq_abi_version.restype = ctypes.c_int
+    lib.awq_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.awq_workspace_bytes.restype = ctypes.c_int64
     if path is None:
         _lib = lib
     return lib
@@ -237,3 +241,60 @@ def w8a8_gemm(qx: torch.Tensor, sx: torch.Tensor, qw: torch.Tensor, sw: torch.Te
 
 def abi_version() -> int:
     return load_library().lq_abi_version()
+
+
+def act_absmean(x: torch.Tensor, sx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sx[k] = mean_t |X[t][k]| (fp32; fp64 sums), AWQ's channel magnitude."""
+    _need(x, "x", torch.bfloat16)
+    t, k = x.shape
+    if sx is None:
+        sx = torch.empty(k, dtype=torch.float32, device=x.device)
+    _need(sx, "sx", torch.float32, (k,))
+    _call("act_absmean", _ptr(x), t, k, _ptr(sx), _stream())
+    return sx
+
+
+@dataclass
+class AwqResult:
+    """Output of awq_search: the packed INT4 weights of W diag(s_best), the
+    chosen scale (to fold 1/s_best into the producer of X), the loss of every
+    grid point and the index of the chosen one (device tensors)."""
+    packed: PackedWeight
+    s_best: torch.Tensor
+    losses: torch.Tensor
+    best: torch.Tensor
+    n_grid: int
+
+
+def awq_search(x: torch.Tensor, w: torch.Tensor, sx: Optional[torch.Tensor] = None, symmetric: bool = False,
+               group: int = 128, n_grid: int = 20, workspace: Optional[torch.Tensor] = None) -> AwqResult:
+    """AWQ scale search over alpha = i / n_grid (see libquant.h); x [t][k] and
+    w [n][k] bf16. sx defaults to act_absmean(x)."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    t, k = x.shape
+    n, kw = w.shape
+    if kw != k:
+        raise ValueError("x and w must share k")
+    if sx is None:
+        sx = act_absmean(x)
+    _need(sx, "sx", torch.float32, (k,))
+    need = load_library().awq_workspace_bytes(t, n, k)
+    if need < 0:
+        raise LibquantError(LQ_ERR_INVALID_ARG, "awq_search", "sizes out of range")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    dev = x.device
+    ng = k // group if group > 0 and k % group == 0 else 0
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, ng), dtype=torch.float32, device=dev)
+    zeros = None if symmetric else torch.empty((n, ng), dtype=torch.float32, device=dev)
+    s_best = torch.empty(k, dtype=torch.float32, device=dev)
+    losses = torch.empty(n_grid + 1, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    _call("awq_search", _ptr(x), t, _ptr(w), n, k, int(bool(symmetric)), group, int(n_grid), _ptr(sx),
+          _ptr(workspace), workspace.numel(), _ptr(s_best), _ptr(losses), _ptr(best), _ptr(codes), _ptr(scales),
+          _ptr(zeros), _stream())
+    return AwqResult(PackedWeight(codes, scales, zeros, n, k, 4, bool(symmetric), group), s_best, losses, best,
+                     int(n_grid))

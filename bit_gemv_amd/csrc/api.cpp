@@ -283,4 +283,65 @@ lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *
     return launched(lq::launch_w8a8_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+lq_status act_absmean(const void *x_bf16, int64_t t, int64_t k, float *sx, void *stream) {
+    const char *fn = "act_absmean";
+    if (t <= 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t and k must be positive (a mean of no tokens)", fn);
+    if (t > kMaxDim || k > kMaxDim || t * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!sx || !aligned(sx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: sx null or not 16-byte aligned", fn);
+    if (any_overlap({{sx, k * 4}}, {{x_bf16, t * k * 2}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps the input", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    return launched(lq::launch_act_absmean(static_cast<const uint16_t *>(x_bf16), t, k, sx,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
+    if (t <= 0 || n <= 0 || k <= 0 || t > kMaxDim || n > kMaxDim || k > kMaxDim || t * n > kMaxElems ||
+        t * k > kMaxElems)
+        return -1;
+    return lq::awq_workspace_bytes(t, n, k);
+}
+
+lq_status awq_search(const void *x_bf16, int64_t t, const void *w_bf16, int64_t n, int64_t k, int symmetric,
+                     int64_t group, int n_grid, const float *sx, void *workspace, int64_t workspace_bytes,
+                     float *s_best, double *losses, int32_t *best, void *codes, float *scales, float *zeros,
+                     void *stream) {
+    const char *fn = "awq_search";
+    if (t <= 0 || n <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t and n must be positive", fn);
+    lq_status st = check_group(fn, k, 4, group);
+    if (st != LQ_OK) return st;
+    if (n_grid < 1 || n_grid > 1024) return fail(LQ_ERR_INVALID_ARG, "%s: n_grid must be in 1..1024", fn);
+    if (t > kMaxDim || n > kMaxDim || t * n > kMaxElems || t * k > kMaxElems || n * k > kMaxElems)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    // the products address 128-row tiles with 32-bit buffer offsets
+    if (k >= (int64_t(1) << 24)) return fail(LQ_ERR_UNSUPPORTED, "%s: k >= 2^24", fn);
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
+    if (!sx || !aligned(sx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: sx null or not 16-byte aligned", fn);
+    const int64_t need = lq::awq_workspace_bytes(t, n, k);
+    if (!workspace || !aligned(workspace, 256))
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+    if (workspace_bytes < need)
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                    (long long)need);
+    if (!s_best || !aligned(s_best, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: s_best null or not 16-byte aligned", fn);
+    if (!losses || !aligned(losses, 8)) return fail(LQ_ERR_INVALID_ARG, "%s: losses null or misaligned", fn);
+    if (!best || !aligned(best, 4)) return fail(LQ_ERR_INVALID_ARG, "%s: best null or misaligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if ((st = check_meta(fn, symmetric, scales, zeros)) != LQ_OK) return st;
+    const int64_t meta = n * (k / group) * 4;
+    if (any_overlap({{workspace, need}, {s_best, k * 4}, {losses, (int64_t)(n_grid + 1) * 8}, {best, 4},
+                     {codes, n * k / 2}, {scales, meta}, {zeros, symmetric ? 0 : meta}},
+                    {{x_bf16, t * k * 2}, {w_bf16, n * k * 2}, {sx, k * 4}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output or the workspace overlaps an input or another output", fn);
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::AwqArgs a{static_cast<const uint16_t *>(x_bf16), t, static_cast<const uint16_t *>(w_bf16), n, k,
+                  symmetric, group, n_grid, sx, workspace, s_best, losses, best,
+                  static_cast<uint8_t *>(codes), scales, zeros};
+    return launched(lq::launch_awq_search(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -65,6 +65,24 @@ struct W8Args {
     float *y;
 };
 
+// AWQ scale search (bits 4): inputs, the caller's workspace and outputs.
+struct AwqArgs {
+    const uint16_t *x;  // calibration activations [t][k]
+    int64_t t;
+    const uint16_t *w;  // weights [n][k]
+    int64_t n, k;
+    int symmetric;
+    int64_t group;
+    int n_grid;
+    const float *sx;    // channel mean magnitudes [k]
+    void *workspace;
+    float *s_best;
+    double *losses;     // [n_grid + 1]
+    int32_t *best;
+    uint8_t *codes;
+    float *scales, *zeros;
+};
+
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
 hipError_t launch_w4a16_gemv(const WoArgs &a, hipStream_t st);
@@ -73,5 +91,8 @@ hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st);
 hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st);
 hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st);
 hipError_t launch_w8a8_gemm(const W8Args &a, hipStream_t st);
+hipError_t launch_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx, hipStream_t st);
+hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st);
+int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
 
 }  // namespace lq

@@ -215,6 +215,55 @@ lq_status quant_per_token_int8(const void *x_bf16, int64_t t, int64_t k, const f
 lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *qw,
                     const float *sw, int64_t n, int64_t k, int32_t *acc, float *y, void *stream);
 
+/*
+ * act_absmean -- the per-channel activation magnitude AWQ scales by
+ * ("3.6 Quantization", AWQ section: s_X, the average activation magnitude of
+ * each input channel over the calibration data; PTQ concept page, AWQ step 1):
+ *   sx[j] = (sum_t |X[t][j]|) / t, summed in fp64, rounded once to fp32.
+ * x_bf16 [t][k] calibration activations (16-byte aligned); sx out fp32 [k]
+ * (16-byte aligned). t, k >= 1.
+ */
+lq_status act_absmean(const void *x_bf16, int64_t t, int64_t k, float *sx, void *stream);
+
+/*
+ * awq_workspace_bytes -- device workspace awq_search needs for these sizes
+ * (two fp32 [t][n] outputs, the bf16 [t][k] scaled activations and small
+ * vectors); -1 for sizes awq_search would reject as too large or empty.
+ */
+int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
+
+/*
+ * awq_search -- AWQ activation-aware scaling with INT4 group-wise RTN
+ * ("3.6 Quantization", AWQ section: scale the weight input channels that
+ * multiply large activations before rounding, y = sum_j (s_j w_j)(x_j / s_j)
+ * -> sum_j quant(s_j w_j) x_j / s_j, with s = s_X^alpha and alpha
+ * grid-searched over [0, 1] per layer for the smallest output error on the
+ * calibration data; 1/s is folded into the preceding operation. PTQ concept
+ * page, AWQ steps 2-5: W' = W diag(s), plain RTN of W'):
+ *   for i = 0 .. n_grid:  alpha_i = i / n_grid
+ *     s_i[j]    = powf(max(sx[j], 1e-8), alpha_i)
+ *     losses[i] = || X W^T - bf16(X / s_i) dequant(quant(W diag(s_i)))^T ||_F^2
+ *                 (X W^T and the quantized product in fp32, the squares
+ *                 summed in fp64)
+ *   best = the first i with the smallest loss; s_best = s_best's s_i; codes,
+ *   scales, zeros = quantize_groupwise(W, 4, symmetric, group, col_scale =
+ *   s_best). A caller folds 1/s_best into the operation that produces X.
+ * x_bf16  [t][k] calibration activations; w_bf16 [n][k] weights; sx [k]
+ *         from act_absmean (16-byte aligned each).
+ * workspace  device memory of at least awq_workspace_bytes(t, n, k) bytes,
+ *         256-byte aligned, owned by the caller, scratch only.
+ * s_best out fp32 [k] (16-byte aligned); losses out fp64 [n_grid + 1];
+ *         best out int32 [1]; codes/scales/zeros out as quantize_groupwise
+ *         with bits = 4 (zeros NULL iff symmetric). All device pointers.
+ * group: multiple of 128 dividing k; k below 2^24; n_grid in 1..1024.
+ * Errors: LQ_ERR_INVALID_ARG for bad sizes, pointers, a short workspace or
+ * overlapping buffers; LQ_ERR_UNSUPPORTED for sizes past the limits above.
+ */
+lq_status awq_search(const void *x_bf16, int64_t t, const void *w_bf16, int64_t n, int64_t k,
+                     int symmetric, int64_t group, int n_grid, const float *sx, void *workspace,
+                     int64_t workspace_bytes, float *s_best, double *losses, int32_t *best, void *codes,
+                     float *scales, float *zeros, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def lib():
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:lq_status|const char \*|int)\s*\*?\s*(\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:lq_status|const char \*|int64_t|int)\s*\*?\s*(\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -147,3 +147,52 @@ def test_smoothquant_entry_points_reject(lib):
 def test_valid_call_without_device_reports_no_device(lib):
     assert _q(lib) == 4
     assert b"no HIP device" in lib.lq_last_error()
+
+
+def test_act_absmean_rejects(lib):
+    assert lib.act_absmean(None, 4, 256, C16, None) == 1
+    assert lib.act_absmean(A16, 0, 256, C16, None) == 1
+    assert lib.act_absmean(A16, 4, 256, MIS, None) == 1
+    assert lib.act_absmean(A16, 4, 256, A16, None) == 1  # sx overlaps x
+
+
+def test_awq_workspace_bytes(lib):
+    assert lib.awq_workspace_bytes(0, 8, 256) == -1
+    assert lib.awq_workspace_bytes(16, 8, -1) == -1
+    # two fp32 [t][n] outputs, bf16 [t][k], fp32 [k], 512 fp64 partials, each 256-aligned
+    assert lib.awq_workspace_bytes(16, 8, 256) == 2 * 512 + 8192 + 1024 + 4096
+
+
+def _awq(lib, x=A16, t=16, w=B16, n=8, k=256, sym=0, group=128, n_grid=20, sx=P(6 << 20), ws=P(7 << 20),
+         ws_bytes=1 << 20, s_best=P(8 << 20), losses=P(9 << 20), best=P(10 << 20), codes=P(11 << 20),
+         scales=P(12 << 20), zeros=P(13 << 20)):
+    return lib.awq_search(x, t, w, n, k, sym, group, n_grid, sx, ws, ws_bytes, s_best, losses, best, codes,
+                          scales, zeros, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(t=0), 1),
+    (dict(n=0), 1),
+    (dict(n_grid=0), 1),
+    (dict(n_grid=2000), 1),
+    (dict(k=300), 1),                          # k not a multiple of group
+    (dict(group=64), 2),
+    (dict(k=1 << 24, group=128), 2),           # past the products' 32-bit tile offsets
+    (dict(x=MIS), 1),
+    (dict(sx=None), 1),
+    (dict(ws=None), 1),
+    (dict(ws=P((7 << 20) + 16)), 1),           # workspace not 256-byte aligned
+    (dict(ws_bytes=1000), 1),                  # workspace too small
+    (dict(sym=1), 1),                          # zeros given for symmetric
+    (dict(zeros=None), 1),                     # zeros missing for asymmetric
+    (dict(ws=P(1 << 20)), 1),                  # workspace overlaps x
+    (dict(codes=P(8 << 20)), 1),               # codes overlap s_best
+])
+def test_awq_search_rejects(lib, kwargs, status):
+    assert _awq(lib, **kwargs) == status
+    assert lib.lq_last_error() != b""
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
+def test_awq_search_valid_call_reports_no_device(lib):
+    assert _awq(lib) == 4
