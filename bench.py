@@ -167,6 +167,48 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
     del packed8
     torch.cuda.empty_cache()
 
+    # f1: AWQ scale search over the Llama-2-7B layer, 512 calibration tokens
+    aw = WORKLOADS["awq7b"]
+    n_grid = aw.extra["n_grid"]
+    lib = bg.load_library()
+    awq = {}
+    xs_k = {}
+    tot_ms = tot_fl = 0.0
+    for i, lin in enumerate(aw.linears):
+        if lin.k not in xs_k:
+            xs_k[lin.k] = dev_bf16(aw.activation(lin.k, aw.tokens))
+        x = xs_k[lin.k]
+        w = dev_bf16(aw.weight(0, i))
+        sx = bg.act_absmean(x)
+        ws = torch.empty(lib.awq_workspace_bytes(aw.tokens, lin.n, lin.k), dtype=torch.uint8, device=dev)
+        out = {}
+
+        def search():
+            out["r"] = bg.awq_search(x, w, sx, aw.symmetric, aw.group, n_grid, workspace=ws)
+
+        ms = _timed(search, reps=3)
+        r = out["r"]
+        losses = r.losses.cpu().numpy()
+        best = int(r.best.cpu()[0])
+        # one reference product and n_grid + 1 quantized products of 2 t n k flops
+        fl = (n_grid + 2) * 2.0 * aw.tokens * lin.n * lin.k
+        tot_ms += ms
+        tot_fl += fl
+        awq[f"{lin.name} {lin.n}x{lin.k}"] = {
+            "ms": round(ms, 3), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1), "best_alpha": best / n_grid,
+            "loss_best_over_rtn": round(float(losses[best] / losses[0]), 4)}
+        log(f"[bench] awq_search {lin.name} {lin.n}x{lin.k}: {ms:.2f} ms, alpha {best / n_grid:.2f}, "
+            f"loss/RTN {losses[best] / losses[0]:.3f}")
+        del w, ws, r, out
+    rows["awq_search"] = {"workload": aw.name, "tokens": aw.tokens, "grid_points": n_grid + 1, "bound": "mfma",
+                          "quant": f"INT4 {'sym' if aw.symmetric else 'asym'} G={aw.group}",
+                          "layer_ms": round(tot_ms, 3),
+                          "layer_TFLOPs": round(tot_fl / (tot_ms * 1e-3) / 1e12, 1),
+                          "frac_of_bf16_peak": round(tot_fl / (tot_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "linears": awq}
+    del xs_k
+    torch.cuda.empty_cache()
+
     # a5: dequantize (fp32 out) of one matrix per layer, across distinct layers
     j = names.index("o") if "o" in names else 0
     n, k = shapes[j]
