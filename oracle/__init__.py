@@ -25,6 +25,10 @@ hold the pins):
   matmul of the codes, the exactness of the smoothing identity and the toy
   error ratio of the code block.
 * ``effective_bits`` / ``packed_bytes``: the printed effective-bit values.
+* ``mx_quantize`` / ``mx_dequantize`` / ``mx_matmul``: the pages' E2M1
+  magnitude table and block size, exact round trips of representable
+  blocks, constructed ties, brute-force nearest-value search, the scale
+  rule at its boundaries, and numpy's matmul on the dequantized weights.
 * ``act_absmean`` / ``awq_scale`` / ``awq_loss`` / ``awq_search``: numpy
   recomputations of the channel means and of the output error from the
   pinned quantizer, the reduction to plain RTN at alpha = 0, and the pages'
@@ -80,6 +84,10 @@ def _load():
         lib.oracle_w4a16_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I64, P]
         lib.oracle_weight_only_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I, I64, P]
         lib.oracle_act_absmean.argtypes = [P, I64, I64, P]
+        lib.oracle_mx_exponent.argtypes = [F]
+        lib.oracle_mx_quantize.argtypes = [P, I64, I64, P, P]
+        lib.oracle_mx_dequantize.argtypes = [P, P, I64, I64, P]
+        lib.oracle_mx_matmul.argtypes = [P, I64, P, P, I64, I64, P]
         lib.oracle_awq_scale.argtypes = [P, I64, I, I, P]
         lib.oracle_awq_scale.restype = None
         lib.oracle_awq_loss.argtypes = [P, I64, P, I64, I64, I, I, I64, P, P]
@@ -286,3 +294,38 @@ def awq_search(x_bf16, w_bf16, bits: int, symmetric: bool, group: int, n_grid: i
     _check(lib.oracle_awq_search(_ptr(x), t, _ptr(w), n, k, bits, int(bool(symmetric)), group, int(n_grid),
                                  _ptr(sx), _ptr(losses), _ptr(best), _ptr(s_best)), "awq_search")
     return sx, losses, int(best[0]), s_best
+
+
+def mx_exponent(amax: float) -> int:
+    """Shared MXFP4 exponent e of a block whose largest magnitude is amax."""
+    return int(_load().oracle_mx_exponent(float(amax)))
+
+
+def mx_quantize(w_bf16):
+    """MXFP4 of bf16 w[n][k] -> (codes uint8 [n][k/2], scales uint8 E8M0 [n][k/32])."""
+    lib = _load()
+    w = _c(w_bf16, np.uint16)
+    n, k = w.shape
+    codes = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, k // 32), np.uint8)
+    _check(lib.oracle_mx_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales)), "mx_quantize")
+    return codes, scales
+
+
+def mx_dequantize(codes, scales, n: int, k: int):
+    lib = _load()
+    out = np.zeros((n, k), np.float32)
+    _check(lib.oracle_mx_dequantize(_ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.uint8)), n, k, _ptr(out)),
+           "mx_dequantize")
+    return out
+
+
+def mx_matmul(x_bf16, codes, scales, n: int, k: int):
+    """y[m][n] = sum_k x[m][k] * x_hat[n][k] in fp64 on MXFP4 weights."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    m = x.shape[0]
+    y = np.zeros((m, n), np.float64)
+    _check(lib.oracle_mx_matmul(_ptr(x), m, _ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.uint8)), n, k, _ptr(y)),
+           "mx_matmul")
+    return y

@@ -556,3 +556,107 @@ out:
     free(y_ref); free(s);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * MXFP4 ([LP] number-format table: FP4 E2M1 elements, magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6, in blocks of 32 sharing one 8-bit power-of-two scale
+ * (E8M0), the OCP Microscaling format, about 4.25 bits per element; [LP]
+ * "Granularity": one scale per block of 32; [CM] "Microscaling (MX)
+ * formats": a block shares an exponent, each element keeps its own bits).
+ * Readings (the pages leave these open):
+ *  - a block is 32 consecutive elements of a row along k;
+ *  - the shared scale is the smallest power of two 2^e with
+ *    amax <= 6 * 2^e (the absmax rule s = amax / qmax restricted to powers
+ *    of two, so no element clips), e clamped to [-127, 127] (E8M0 = e + 127;
+ *    an all-zero block takes e = -127);
+ *  - each element is x / 2^e rounded to the nearest E2M1 magnitude, ties to
+ *    the even encoding (mantissa bit 0), with the sign of x; a zero
+ *    magnitude is stored as +0;
+ *  - codes pack two per byte, element 2j in the low nibble (as INT4);
+ *    the E2M1 nibble is sign << 3 | exponent << 1 | mantissa.
+ * ---------------------------------------------------------------------- */
+static const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* The shared exponent of a block with largest magnitude amax. */
+int oracle_mx_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return -127;
+    int p;
+    const float m = frexpf(amax, &p);      /* amax = m 2^p, m in [0.5, 1) */
+    int e = p - 3 + (m > 0.75f ? 1 : 0);    /* smallest e with amax <= 1.5 * 2^(e + 2) */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Nearest E2M1 magnitude index of a magnitude v in [0, 6], ties to even. */
+static int e2m1_round(float v)
+{
+    int best = 0;
+    for (int i = 1; i < 8; ++i) {
+        const float d = fabsf(v - kE2M1[i]), db = fabsf(v - kE2M1[best]);
+        if (d < db || (d == db && (i & 1) == 0)) best = i;
+    }
+    return best;
+}
+
+/* w: bf16 bits [n][k] (k a multiple of 32); codes [n][k/2]; scales [n][k/32] (E8M0). */
+int oracle_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales)
+{
+    if (n < 0 || k <= 0 || k % 32 != 0) return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const uint16_t *x = w + r * k + b * 32;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                const float a = fabsf(bf16_bits_to_f32(x[j]));
+                if (a > amax) amax = a;
+            }
+            const int e = oracle_mx_exponent(amax);
+            scales[r * (k / 32) + b] = (uint8_t)(e + 127);
+            uint8_t nib[32];
+            for (int j = 0; j < 32; ++j) {
+                const float v = bf16_bits_to_f32(x[j]);
+                const int mag = e2m1_round(fabsf(ldexpf(v, -e)));
+                nib[j] = (uint8_t)(mag == 0 ? 0 : ((v < 0.0f ? 8 : 0) | mag));
+            }
+            for (int j = 0; j < 32; j += 2)
+                codes[r * (k / 2) + b * 16 + j / 2] = (uint8_t)(nib[j] | (nib[j + 1] << 4));
+        }
+    return 0;
+}
+
+/* x_hat = (+-E2M1) * 2^e, exact in fp32. out: [n][k]. */
+int oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, float *out)
+{
+    if (n < 0 || k <= 0 || k % 32 != 0) return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = 0; j < k; ++j) {
+            const uint8_t byte = codes[r * (k / 2) + j / 2];
+            const int c = (j & 1) ? byte >> 4 : byte & 0xF;
+            const int e = (int)scales[r * (k / 32) + j / 32] - 127;
+            const float mag = ldexpf(kE2M1[c & 7], e);
+            out[r * k + j] = (c & 8) ? -mag : mag;
+        }
+    return 0;
+}
+
+/* MXFP4 weights with 16-bit activations: y[i][r] = sum_j x[i][j] x_hat[r][j]
+ * in fp64 (the weight-only product of the W4A16 rows with MXFP4 weights). */
+int oracle_mx_matmul(const uint16_t *x, int64_t m, const uint8_t *codes, const uint8_t *scales, int64_t n,
+                     int64_t k, double *y)
+{
+    if (m < 0 || n < 0 || k <= 0 || k % 32 != 0) return -1;
+    float *wrow = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!wrow) return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        oracle_mx_dequantize(codes + r * (k / 2), scales + r * (k / 32), 1, k, wrow);
+        for (int64_t i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j) acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];
+            y[i * n + r] = acc;
+        }
+    }
+    free(wrow);
+    return 0;
+}

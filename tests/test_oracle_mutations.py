@@ -48,6 +48,13 @@ MUTANTS = {
                              "if (oracle_quantize_bf16(w, n, k, bits, symmetric, group, NULL, codes, sc, zr)) goto out;"),
     "awq_argmax": ("if (losses[i] < losses[arg]) arg = i;", "if (losses[i] > losses[arg]) arg = i;"),
     "awq_abs_error": ("total += d * d;", "total += fabs(d);"),
+    "mx_ties_to_odd": ("if (d < db || (d == db && (i & 1) == 0)) best = i;",
+                       "if (d < db || (d == db && (i & 1) == 1)) best = i;"),
+    "mx_scale_floor_clips": ("int e = p - 3 + (m > 0.75f ? 1 : 0);", "int e = p - 3;"),
+    "mx_nibble_order": ("codes[r * (k / 2) + b * 16 + j / 2] = (uint8_t)(nib[j] | (nib[j + 1] << 4));",
+                        "codes[r * (k / 2) + b * 16 + j / 2] = (uint8_t)(nib[j + 1] | (nib[j] << 4));"),
+    "mx_negative_zero_kept": ("nib[j] = (uint8_t)(mag == 0 ? 0 : ((v < 0.0f ? 8 : 0) | mag));",
+                              "nib[j] = (uint8_t)((v < 0.0f ? 8 : 0) | mag);"),
     "smooth_inverted": ("s[j] = sqrtf(a) / sqrtf(b);", "s[j] = sqrtf(b) / sqrtf(a);"),
     "smooth_alpha_swapped": ("s[j] = powf(a, alpha) / powf(b, 1.0f - alpha);",
                              "s[j] = powf(a, 1.0f - alpha) / powf(b, alpha);"),

@@ -581,3 +581,131 @@ def test_awq_scaling_shrinks_a_channels_error_about_1_over_s():
         return np.abs(w_hat[:, 5] / cs[5] - w[:, 5]).mean()
     e1, e4 = err(np.ones(k, f32)), err(s)
     assert 0.18 < e4 / e1 < 0.32
+
+
+# --------------------------------------------------------------------------
+# MXFP4 (number-format table of "3.6 Quantization"; compendium MX formats).
+# --------------------------------------------------------------------------
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mx_block_rows(vals):
+    """bf16 bits of a [rows][32k] float array (values must be exact in bf16)."""
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    a = np.asarray(vals, np.float32)
+    h = f32_to_bf16_bits(a)
+    assert np.array_equal(bf16_bits_to_f32(h), a)
+    return h
+
+
+def _nibbles(codes, k):
+    lo = (codes & 0xF).astype(np.int32)
+    hi = (codes >> 4).astype(np.int32)
+    out = np.empty((codes.shape[0], k), np.int32)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return out
+
+
+def test_mx_e2m1_table_is_the_pages(golden):
+    """Codes 0..7 with a unit scale decode to the printed E2M1 magnitudes,
+    8..15 to their negatives; the largest is 6; a 32-block with an 8-bit
+    scale costs 4.25 bits per element."""
+    _, p = golden
+    t = p["fp4_e2m1"]
+    codes = np.array([[c | (c + 1) << 4 for c in range(0, 16, 2)] * 2], np.uint8)  # 32 nibbles 0..15, 0..15
+    out = oracle.mx_dequantize(codes, np.array([[127]], np.uint8), 1, 32)[0]
+    assert np.array_equal(out[:8], np.array(t["magnitudes"], f32))
+    assert np.array_equal(out[8:16], -np.array(t["magnitudes"], f32))
+    assert out.max() == t["max"] and t["block"] == 32
+    assert oracle.effective_bits(4, t["scale_bits"], 0, t["block"]) == t["bits_per_element"]
+
+
+def test_mx_exponent_is_the_smallest_fitting_power_of_two():
+    """e is the smallest integer with amax <= 6 * 2^e (checked by brute force
+    in exact arithmetic), clamped to the E8M0 range."""
+    import math
+    rng = np.random.default_rng(40)
+    cases = [6.0, 3.0, 1.5, 0.75, 1.0, 7.0, 12.0, 2.0 ** -100, 1e-45, 3e38]
+    for e in (-126, -20, -1, 0, 5, 100):
+        v = math.ldexp(6.0, e)
+        cases += [v, float(np.nextafter(f32(v), f32(np.inf))), float(np.nextafter(f32(v), f32(0)))]
+    cases += list(np.exp(rng.uniform(-60, 60, 200)))
+    for a in cases:
+        a = float(f32(a))
+        got = oracle.mx_exponent(a)
+        e = -200
+        while math.ldexp(6.0, e) < a:
+            e += 1
+        assert got == max(-127, min(127, e)), (a, got, e)
+    assert oracle.mx_exponent(0.0) == -127
+
+
+def test_mx_round_trip_of_representable_blocks():
+    """Blocks of +-E2M1 * 2^e containing 6 * 2^e come back exactly."""
+    rng = np.random.default_rng(41)
+    for e in (-30, -3, 0, 2, 40):
+        vals = rng.choice(E2M1, (3, 64)) * rng.choice([-1.0, 1.0], (3, 64))
+        vals[:, 0], vals[:, 32] = 6.0, -6.0
+        vals = np.ldexp(vals, e)
+        w = _mx_block_rows(vals)
+        codes, scales = oracle.mx_quantize(w)
+        assert np.all(scales == e + 127)
+        assert np.array_equal(oracle.mx_dequantize(codes, scales, 3, 64), vals.astype(f32))
+
+
+def test_mx_ties_go_to_the_even_encoding():
+    """Half-way values between neighbouring magnitudes: 0.25 -> 0, 0.75 -> 1,
+    1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4 (even = mantissa bit 0)."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    row = np.zeros(32)
+    row[0] = 6.0
+    row[1:8] = mids
+    row[8:15] = [-m for m in mids]
+    out = oracle.mx_dequantize(*oracle.mx_quantize(_mx_block_rows([row])), 1, 32)[0]
+    assert list(out[1:8]) == want
+    assert list(out[8:15]) == [-v if v else 0.0 for v in want]
+
+
+def test_mx_brute_force_nearest_and_zero_sign():
+    """Random blocks: every element is the nearest signed grid value times
+    2^e (ties to the even encoding), zeros are stored as +0 codes, and the
+    error is at most 2^e."""
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((40, 256)) * np.exp(rng.uniform(-8, 8, (40, 1)))
+    x[3, :32] = 0.0
+    x[4, 5] = -1e-30
+    w = f32_to_bf16_bits(x)
+    xf = bf16_bits_to_f32(w).astype(np.float64)
+    codes, scales = oracle.mx_quantize(w)
+    out = oracle.mx_dequantize(codes, scales, 40, 256).astype(np.float64)
+    nib = _nibbles(codes, 256)
+    e = scales.astype(np.int64).repeat(32, axis=1) - 127
+    v = np.ldexp(xf, -e)
+    grid = np.concatenate([-E2M1[::-1], E2M1])          # -6 .. 6
+    enc = np.concatenate([np.arange(7, -1, -1), np.arange(8)])
+    d = np.abs(v[..., None] - grid)
+    dmin = d.min(-1)
+    assert np.all(dmin <= 1.0)
+    q = np.ldexp(out, -e)
+    for idx in zip(*np.nonzero(np.abs(np.abs(v - q) - dmin) > 0)):
+        raise AssertionError(f"not nearest at {idx}")
+    tie = (np.isclose(d, dmin[..., None], rtol=0, atol=0)).sum(-1) > 1
+    assert np.all((np.abs(q[tie]) == 0) | ((enc[np.searchsorted(grid, q[tie])] & 1) == 0))
+    assert np.all(nib[out == 0] == 0)
+    assert np.all(np.abs(out - xf) <= np.ldexp(1.0, e) + 0.0)
+
+
+def test_mx_matmul_is_x_times_dequantized_transpose():
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(43)
+    n, k, m = 17, 320, 3
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    x = f32_to_bf16_bits(rng.standard_normal((m, k)))
+    codes, scales = oracle.mx_quantize(w)
+    y = oracle.mx_matmul(x, codes, scales, n, k)
+    ref = bf16_bits_to_f32(x).astype(np.float64) @ oracle.mx_dequantize(codes, scales, n, k).astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    full = bf16_bits_to_f32(x).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
+    assert np.linalg.norm(y - full) / np.linalg.norm(full) < 0.2
