@@ -647,16 +647,16 @@ int oracle_mx_matmul(const uint16_t *x, int64_t m, const uint8_t *codes, const u
                      int64_t k, double *y)
 {
     if (m < 0 || n < 0 || k <= 0 || k % 32 != 0) return -1;
-    float *wrow = (float *)malloc(sizeof(float) * (size_t)k);
-    if (!wrow) return -1;
+    float *mrow = (float *)malloc(sizeof(float) * (size_t)k);
+    if (!mrow) return -1;
     for (int64_t r = 0; r < n; ++r) {
-        oracle_mx_dequantize(codes + r * (k / 2), scales + r * (k / 32), 1, k, wrow);
+        oracle_mx_dequantize(codes + r * (k / 2), scales + r * (k / 32), 1, k, mrow);
         for (int64_t i = 0; i < m; ++i) {
             double acc = 0.0;
-            for (int64_t j = 0; j < k; ++j) acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)wrow[j];
+            for (int64_t j = 0; j < k; ++j) acc += (double)bf16_bits_to_f32(x[i * k + j]) * (double)mrow[j];
             y[i * n + r] = acc;
         }
     }
-    free(wrow);
+    free(mrow);
     return 0;
 }
