@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libquant.so")
 LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = range(5)
 
 ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w8a16_gemv", "w4a16_gemm",
-                "smooth_scale", "quant_per_token_int8", "w8a8_gemm", "act_absmean", "awq_search")
+                "smooth_scale", "quant_per_token_int8", "w8a8_gemm", "act_absmean", "awq_search",
+                "mxfp4_quantize", "mxfp4_gemv")
 
 
 class LibquantError(RuntimeError):
@@ -59,6 +60,8 @@ def load_library(path: Optional[str] = None):
         "quant_per_token_int8": [P, I64, I64, P, P, P, P],
         "w8a8_gemm": [P, P, I64, P, P, I64, I64, P, P, P],
         "act_absmean": [P, I64, I64, P, P],
+        "mxfp4_quantize": [P, I64, I64, P, P, P],
+        "mxfp4_gemv": [P, I64, P, P, I64, I64, P, P],
         "awq_search": [P, I64, P, I64, I64, I, I64, I, P, P, I64, P, P, P, P, P, P, P],
     }
     for name, argtypes in sigs.items():
@@ -298,3 +301,39 @@ def awq_search(x: torch.Tensor, w: torch.Tensor, sx: Optional[torch.Tensor] = No
           _ptr(zeros), _stream())
     return AwqResult(PackedWeight(codes, scales, zeros, n, k, 4, bool(symmetric), group), s_best, losses, best,
                      int(n_grid))
+
+
+@dataclass
+class MxWeight:
+    """Output of mxfp4_quantize: E2M1 codes [n][k/2] and E8M0 block scales [n][k/32]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    n: int
+    k: int
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel()
+
+
+def mxfp4_quantize(w: torch.Tensor, out: Optional[MxWeight] = None) -> MxWeight:
+    """MXFP4 of bf16 W[n][k]: blocks of 32 along k (see libquant.h)."""
+    _need(w, "w", torch.bfloat16)
+    n, k = w.shape
+    if out is None:
+        out = MxWeight(torch.empty((n, k // 2), dtype=torch.uint8, device=w.device),
+                       torch.empty((n, k // 32), dtype=torch.uint8, device=w.device), n, k)
+    _call("mxfp4_quantize", _ptr(w), n, k, _ptr(out.codes), _ptr(out.scales), _stream())
+    return out
+
+
+def mxfp4_gemv(x: torch.Tensor, mw: MxWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[b][n] = x[b][k] W_hat^T on MXFP4 weights, b <= 16 (fp32 out)."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    if k != mw.k:
+        raise ValueError(f"x has {k} columns, weights have k = {mw.k}")
+    if y is None:
+        y = torch.empty((m, mw.n), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, mw.n))
+    _call("mxfp4_gemv", _ptr(x), m, _ptr(mw.codes), _ptr(mw.scales), mw.n, mw.k, _ptr(y), _stream())
+    return y

@@ -283,6 +283,49 @@ lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *
     return launched(lq::launch_w8a8_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+lq_status mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, void *codes, void *scales, void *stream) {
+    const char *fn = "mxfp4_quantize";
+    if (n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: n must be >= 0 and k > 0", fn);
+    if (k % 32 != 0) return fail(LQ_ERR_INVALID_ARG, "%s: k (%lld) is not a multiple of the block of 32", fn,
+                                 (long long)k);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (n > kMaxDim || k > kMaxDim || n * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: matrix too large", fn);
+    if (n == 0) return LQ_OK;
+    if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (!scales || !aligned(scales, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: scales null or not 16-byte aligned", fn);
+    if (any_overlap({{codes, n * k / 2}, {scales, n * k / 32}}, {{w_bf16, n * k * 2}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output overlaps the input or the other output", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    return launched(lq::launch_mx_quantize(static_cast<const uint16_t *>(w_bf16), n, k, static_cast<uint8_t *>(codes),
+                                           static_cast<uint8_t *>(scales), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const void *scales, int64_t n, int64_t k,
+                     float *y, void *stream) {
+    const char *fn = "mxfp4_gemv";
+    if (b < 0 || n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size or k <= 0", fn);
+    if (b > 16) return fail(LQ_ERR_UNSUPPORTED, "%s: batch %lld > 16", fn, (long long)b);
+    if (k % 32 != 0) return fail(LQ_ERR_INVALID_ARG, "%s: k (%lld) is not a multiple of the block of 32", fn,
+                                 (long long)k);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (n > kMaxDim || k > (int64_t(1) << 28)) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    if (b == 0 || n == 0) return LQ_OK;
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (!scales || !aligned(scales, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: scales null or not 16-byte aligned", fn);
+    if (!y || !aligned(y, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: y null or not 16-byte aligned", fn);
+    if (any_overlap({{y, b * n * 4}}, {{x_bf16, b * k * 2}, {codes, n * k / 2}, {scales, n * k / 32}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::MxArgs a{static_cast<const uint16_t *>(x_bf16), b, static_cast<const uint8_t *>(codes),
+                 static_cast<const uint8_t *>(scales), n, k, y};
+    return launched(lq::launch_mx_gemv(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 lq_status act_absmean(const void *x_bf16, int64_t t, int64_t k, float *sx, void *stream) {
     const char *fn = "act_absmean";
     if (t <= 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t and k must be positive (a mean of no tokens)", fn);

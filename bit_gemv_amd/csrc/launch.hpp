@@ -65,6 +65,16 @@ struct W8Args {
     float *y;
 };
 
+// MXFP4 weights (E2M1 codes, E8M0 block scales) with bf16 activations.
+struct MxArgs {
+    const uint16_t *x;
+    int64_t m;
+    const uint8_t *codes;
+    const uint8_t *scales;
+    int64_t n, k;
+    float *y;
+};
+
 // AWQ scale search (bits 4): inputs, the caller's workspace and outputs.
 struct AwqArgs {
     const uint16_t *x;  // calibration activations [t][k]
@@ -91,6 +101,9 @@ hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st);
 hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st);
 hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st);
 hipError_t launch_w8a8_gemm(const W8Args &a, hipStream_t st);
+hipError_t launch_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales,
+                              hipStream_t st);
+hipError_t launch_mx_gemv(const MxArgs &a, hipStream_t st);
 hipError_t launch_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx, hipStream_t st);
 hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st);
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);

@@ -1,0 +1,245 @@
+// mx.hip -- MXFP4 weights on gfx950: the block quantizer and the decode GEMV
+// with 16-bit activations.
+//
+// Format ("3.6 Quantization", number-format table: FP4 E2M1 elements with
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, in blocks of 32 sharing one 8-bit
+// power-of-two scale, E8M0, as in the OCP Microscaling standard; "Granularity":
+// one scale per block of 32; compendium "Microscaling (MX) formats": a block
+// shares an exponent, each element keeps its own bits). Readings where the
+// pages leave a step open:
+//  - a block is 32 consecutive elements of a row along k;
+//  - the shared scale 2^e is the smallest power of two with amax <= 6 * 2^e
+//    (the absmax rule restricted to powers of two: no element clips), e
+//    clamped to [-127, 127], stored as the E8M0 byte e + 127 (an all-zero
+//    block stores 0);
+//  - an element is x / 2^e rounded to the nearest E2M1 magnitude, ties to
+//    the even encoding, with the sign of x; a zero magnitude is stored +0;
+//  - two codes per byte, element 2j in the low nibble; the nibble is
+//    sign << 3 | exponent << 1 | mantissa.
+// The GEMV: y[b][r] = sum_j x[b][j] * E2M1(c[r][j]) * 2^e[r][j/32].
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lq {
+
+namespace {
+
+// e = smallest integer with amax <= 6 * 2^e = 1.5 * 2^(e + 2), from the bits
+// of amax: amax = f * 2^E with f in [1, 2) gives e = E - 2 + (f > 1.5).
+LQ_DEVICE int mx_exponent(float amax) {
+    // zero and subnormal amax (below 2^-126) land below the E8M0 range: -127
+    const uint32_t u = __float_as_uint(amax);
+    if ((u >> 23) == 0) return -127;
+    const int e = (int)(u >> 23) - 127 - 2 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Nearest E2M1 magnitude index of a in [0, 6]; at a tie the neighbour with
+// the even encoding wins (midpoints 0.25, 1.25, 2.5, 5 stay down, 0.75,
+// 1.75, 3.5 go up).
+LQ_DEVICE uint32_t e2m1_index(float a) {
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+           (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+}
+
+LQ_DEVICE uint32_t e2m1_code(float x, int e) {
+    const float v = __builtin_amdgcn_ldexpf(x, -e);  // exact unless below the fp32 normal range (then 0)
+    const uint32_t mag = e2m1_index(fabsf(v));
+    return mag == 0 ? 0u : (mag | (x < 0.0f ? 8u : 0u));
+}
+
+// One lane quantizes 8 elements (16 bytes of bf16); 4 lanes form a block of
+// 32. The matrix is flattened: k is a multiple of 32, so blocks never span
+// rows and block b covers elements [32 b, 32 b + 32), code bytes
+// [16 b, 16 b + 16) and scale byte b.
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restrict__ w, int64_t total8,
+                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // lanes past the end take part in the 4-lane maximum with zeros
+    const bool in = i < total8;
+    const u32x4 v = in ? reinterpret_cast<const u32x4 *>(w)[i] : u32x4{0u, 0u, 0u, 0u};
+    float xs[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                   bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(xs[j]));
+    // maximum over the block's 4 lanes (aligned quads of the wave)
+    a = fmaxf(a, dpp_move<kDppXor1>(a));
+    a = fmaxf(a, dpp_move<kDppXor2>(a));
+    const int e = mx_exponent(a);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) packed |= e2m1_code(xs[j], e) << (4 * j);
+    if (in) {
+        reinterpret_cast<uint32_t *>(codes)[i] = packed;
+        if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV, batch 1..16 (VALU). A lane owns 32 consecutive k of a row -- one
+// 16-byte code load and exactly one MX block -- so a wave load covers 2048 k.
+// v_cvt_scalef32_pk_bf16_fp4 turns each code byte into the exact bf16 pair
+// (E2M1 of the low nibble, E2M1 of the high nibble), which is the natural k
+// order of the activation word holding the same two k; v_dot2_f32_bf16
+// multiplies them (products exact in fp32) and the block's 2^e scales the
+// lane's sum once, exactly, in fp32. Block layout as the INT4 kernel: 4
+// waves split the chunks of k (ks_count ways) and the block's rows; the
+// 64 scale bytes of each of a wave's rows per chunk come from one 16-byte
+// load per lane (lanes 0 .. 4 RW - 1), passed through the wave's LDS slice.
+// ---------------------------------------------------------------------------
+constexpr int kMxChunk = 2048;
+
+// 2^(s - 127) for an E8M0 byte s (s = 0 is the subnormal 2^-127)
+LQ_DEVICE float e8m0_value(uint32_t s) { return __uint_as_float(s ? s << 23 : 0x00400000u); }
+
+template <int B, int RW>
+__global__ __launch_bounds__(256) void mx_gemv_kernel(const uint16_t *__restrict__ x, int bsz,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales, int n, int k,
+                                                      int ks_count, float *__restrict__ y) {
+    static_assert(RW == 4 || RW == 8, "rows per wave: 4 or 8");
+    static_assert(RW * B <= 64, "the final sum gives one output per lane");
+    __shared__ float red[4][B][RW];
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[4][RW][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks_log = ks_count == 4 ? 2 : ks_count - 1;
+    const int ks = wave & (ks_count - 1);
+    const int rs = wave >> ks_log;
+    const int row0 = (blockIdx.x * (4 >> ks_log) + rs) * RW;
+    const int nblk = k / 32;
+    const int nchunks = (k + kMxChunk - 1) / kMxChunk;
+    const int rows_here = row0 < n ? min(RW, n - row0) : 0;
+    const uint32_t row_bytes = (uint32_t)k / 2;
+    const auto rc = make_rsrc(codes + (int64_t)row0 * row_bytes, (uint32_t)rows_here * row_bytes);
+    const auto rsc = make_rsrc(scales + (int64_t)row0 * nblk, (uint32_t)(rows_here * nblk));
+
+    float acc[B][RW];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[b][r] = 0.0f;
+
+    for (int c = ks; c < nchunks; c += ks_count) {
+        const int k0 = c * kMxChunk + lane * 32;
+        const bool kv = k0 < k;
+        u32x4 xv[B][4];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const auto rx = make_rsrc(x + (int64_t)b * k, b < bsz ? (uint32_t)k * 2 : 0u);
+            const uint32_t xo = kv ? (uint32_t)k0 * 2 : kOutOfRange;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * j, 0, 0);
+        }
+        const uint32_t co = kv ? (uint32_t)k0 / 2 : kOutOfRange;
+        u32x4 cw[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+            cw[r] = __builtin_amdgcn_raw_buffer_load_b128(rc, co + r * row_bytes, 0, kNonTemporal);
+        // scale bytes: lane L < 4 RW loads row L / 4, bytes 16 (L % 4) .. + 15 of the chunk
+        const int sr = lane >> 2, sq = lane & 3;
+        const int sb = c * (kMxChunk / 32) + 16 * sq;
+        const uint32_t so = sr < RW && sb < nblk ? (uint32_t)(sr * nblk + sb) : kOutOfRange;
+        const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rsc, so, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (sr < RW) *reinterpret_cast<u32x4 *>(&sc_lds[wave][sr][16 * sq]) = sv;
+        // one wave writes and reads its slice: LDS runs them in order; keep
+        // the compiler from moving the reads above the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float sc[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) sc[r] = kv ? e8m0_value(sc_lds[wave][r][lane]) : 0.0f;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const uint32_t cwv[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+            uint32_t p[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                p[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 0));
+                p[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 1));
+                p[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 2));
+                p[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 3));
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float d = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    d = dot2_bf16(p[4 * j + 0], xv[b][j].x, d);
+                    d = dot2_bf16(p[4 * j + 1], xv[b][j].y, d);
+                    d = dot2_bf16(p[4 * j + 2], xv[b][j].z, d);
+                    d = dot2_bf16(p[4 * j + 3], xv[b][j].w, d);
+                }
+                acc[b][r] = __builtin_fmaf(d, sc[r], acc[b][r]);
+            }
+        }
+    }
+    constexpr int P = RW == 4 ? 2 : 3;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float v = reduce_rows<RW>(acc[b], lane);
+        if ((lane & ((64 >> P) - 1)) == 0) red[wave][b][lane >> (6 - P)] = v;
+    }
+    __syncthreads();
+    if (ks == 0 && lane < RW * B) {
+        const int b = lane / RW, r = lane % RW;
+        float v = 0.0f;
+        for (int w = 0; w < ks_count; ++w) v += red[rs * ks_count + w][b][r];
+        const int row = row0 + r;
+        if (row < n && b < bsz) y[(int64_t)b * n + row] = v;
+    }
+}
+
+template <int B, int RW>
+hipError_t launch_mx_rw(const MxArgs &a, hipStream_t st, int ks_count) {
+    const int rows_per_block = (4 / ks_count) * RW;
+    const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((mx_gemv_kernel<B, RW>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x, (int)a.m, a.codes,
+                       a.scales, (int)a.n, (int)a.k, ks_count, a.y);
+    return hipGetLastError();
+}
+
+// Launch shape as the INT4 kernel (same code bytes per chunk): k split 4
+// ways at 4..7 chunks a row, 2 ways at 2..3 or 8 and more; 8 rows a wave
+// while that leaves 512 blocks and the batch allows it.
+template <int B>
+hipError_t launch_mx(const MxArgs &a, hipStream_t st) {
+    const int nchunks = (int)((a.k + kMxChunk - 1) / kMxChunk);
+    const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
+    const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
+    if constexpr (B <= 8) {
+        if (blocks8 >= 512) return launch_mx_rw<B, 8>(a, st, ks);
+    }
+    return launch_mx_rw<B, 4>(a, st, ks);
+}
+
+}  // namespace
+
+hipError_t launch_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales,
+                              hipStream_t st) {
+    const int64_t total8 = n * k / 8;
+    hipLaunchKernelGGL(mx_quant_kernel, dim3((uint32_t)((total8 + 255) / 256)), dim3(256), 0, st, w, total8, codes,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_gemv(const MxArgs &a, hipStream_t st) {
+    switch (a.m) {
+        case 1: return launch_mx<1>(a, st);
+        case 2: return launch_mx<2>(a, st);
+        case 3: return launch_mx<3>(a, st);
+        case 4: return launch_mx<4>(a, st);
+        default:
+            if (a.m <= 8) return launch_mx<8>(a, st);
+            if (a.m <= 16) return launch_mx<16>(a, st);
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lq

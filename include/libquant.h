@@ -216,6 +216,38 @@ lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *
                     const float *sw, int64_t n, int64_t k, int32_t *acc, float *y, void *stream);
 
 /*
+ * mxfp4_quantize -- MXFP4 block quantization ("3.6 Quantization", number-
+ * format table: FP4 E2M1 elements, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, in
+ * blocks of 32 sharing an 8-bit power-of-two scale, E8M0, OCP Microscaling;
+ * "Granularity": one scale per block of 32; compendium "Microscaling (MX)
+ * formats"). Per block of 32 consecutive elements of a row:
+ *   e = the smallest integer with max|w| <= 6 * 2^e, clamped to [-127, 127]
+ *       (an all-zero block gives -127); scales[.] = e + 127 (E8M0 byte)
+ *   c = the E2M1 value nearest to w / 2^e (ties to the even encoding), with
+ *       the sign of w; a zero magnitude is stored as +0.
+ * w_bf16 [n][k]; codes out [n][k/2] (nibble sign << 3 | exponent << 1 |
+ * mantissa, element 2j in the low nibble of byte j); scales out uint8
+ * [n][k/32]. All 16-byte aligned. k multiple of 128 (a multiple of 32 that
+ * is not: LQ_ERR_UNSUPPORTED; not a multiple of 32: LQ_ERR_INVALID_ARG).
+ * Magnitudes above 6 * 2^126 leave the fp32 range when dequantized and are
+ * outside the contract.
+ */
+lq_status mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, void *codes, void *scales,
+                         void *stream);
+
+/*
+ * mxfp4_gemv -- batch-b decode product with MXFP4 weights and 16-bit
+ * activations (the weight-only product of "LLM quantization deep dive",
+ * W4A16, with the MXFP4 weights above):
+ *   y[i][r] = sum_j x[i][j] * E2M1(c[r][j]) * 2^(scales[r][j/32] - 127)
+ * x_bf16 [b][k], b in 0..16 (larger: LQ_ERR_UNSUPPORTED); codes, scales as
+ * mxfp4_quantize writes them; y out fp32 [b][n]. 16-byte aligned; k multiple
+ * of 128 and at most 2^28.
+ */
+lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const void *scales,
+                     int64_t n, int64_t k, float *y, void *stream);
+
+/*
  * act_absmean -- the per-channel activation magnitude AWQ scales by
  * ("3.6 Quantization", AWQ section: s_X, the average activation magnitude of
  * each input channel over the calibration data; PTQ concept page, AWQ step 1):

@@ -196,3 +196,16 @@ def test_awq_search_rejects(lib, kwargs, status):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: valid calls would launch")
 def test_awq_search_valid_call_reports_no_device(lib):
     assert _awq(lib) == 4
+
+
+def test_mxfp4_entry_points_reject(lib):
+    assert lib.mxfp4_quantize(A16, 4, 100, B16, C16, None) == 1      # k not a multiple of 32
+    assert lib.mxfp4_quantize(A16, 4, 96, B16, C16, None) == 2       # a multiple of 32, not of 128
+    assert lib.mxfp4_quantize(MIS, 4, 256, B16, C16, None) == 1
+    assert lib.mxfp4_quantize(A16, 4, 256, B16, P((2 << 20) + 64), None) == 1  # scales overlap codes
+    assert lib.mxfp4_quantize(None, 0, 256, None, None, None) == 0
+    assert lib.mxfp4_gemv(A16, 17, B16, C16, 8, 256, D16, None) == 2
+    assert lib.mxfp4_gemv(A16, 1, B16, C16, 8, 200, D16, None) == 1
+    assert lib.mxfp4_gemv(A16, 1, B16, MIS, 8, 256, D16, None) == 1
+    assert lib.mxfp4_gemv(A16, 1, B16, C16, 8, 256, A16, None) == 1  # y aliases x
+    assert lib.mxfp4_gemv(A16, 0, B16, C16, 8, 256, D16, None) == 0

@@ -1,0 +1,111 @@
+"""MXFP4 quantizer (bit-exact) and MXFP4 x bf16 GEMV (fp64 oracle) on the GPU."""
+import numpy as np
+import pytest
+
+import bit_gemv_amd as bg
+import oracle
+from gpu_helpers import assert_close, assert_same_bits, dev_bf16, host, say
+from workloads import WORKLOADS, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_check(w, what):
+    n, k = w.shape
+    say(f"mxfp4_quantize {what} n={n} k={k}")
+    mw = bg.mxfp4_quantize(dev_bf16(w))
+    c_ref, s_ref = oracle.mx_quantize(w)
+    assert_same_bits(host(mw.scales), s_ref, f"{what} scales")
+    assert_same_bits(host(mw.codes), c_ref, f"{what} codes")
+    return mw, c_ref, s_ref
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (7, 384), (300, 4096), (4096 + 3, 11008)])
+def test_quantize_random_rows(n, k):
+    """Rows spread over 2^-40 .. 2^40 so blocks take many exponents."""
+    rng = np.random.default_rng(n + k)
+    w = rng.standard_normal((n, k)) * np.exp(rng.uniform(-28, 28, (n, 1)))
+    _quant_check(f32_to_bf16_bits(w), "random")
+
+
+def test_quantize_every_finite_bf16_value():
+    """All finite bf16 bit patterns, in order, 32 to a block (each block holds
+    neighbouring patterns, so every value meets scales near its own), plus the
+    same patterns shuffled across blocks."""
+    pats = np.arange(65536, dtype=np.uint32)
+    exp = (pats >> 7) & 0xFF
+    finite = pats[exp != 0xFF].astype(np.uint16)
+    pad = (-finite.size) % 4096
+    allv = np.concatenate([finite, np.zeros(pad, np.uint16)]).reshape(-1, 4096)
+    _quant_check(allv, "every bf16 (ordered)")
+    rng = np.random.default_rng(5)
+    _quant_check(rng.permutation(allv.ravel()).reshape(allv.shape), "every bf16 (shuffled)")
+
+
+def test_quantize_ties_zeros_and_tiny_blocks():
+    rng = np.random.default_rng(6)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = []
+    for e in (-127, -126, -20, 0, 13, 120):
+        r = np.zeros(128)
+        r[0] = 6.0
+        r[1:8], r[8:15] = mids, -mids
+        r[32:64] = rng.choice([0.5, 1.0, 1.5, 3.0, 6.0], 32) * rng.choice([-1, 1], 32)
+        r[64] = 6.0
+        r[96:128] = 0.0                                # an all-zero block
+        rows.append(np.ldexp(r, e))
+    w = f32_to_bf16_bits(np.array(rows, np.float32))
+    w[0, 100] = 0x8000                                 # -0.0 in the zero block
+    w[1, 101] = 0x0001                                 # the smallest subnormal bf16
+    _quant_check(w, "ties/zeros")
+
+
+def _gemv_case(n, k, b, seed, what=""):
+    rng = np.random.default_rng(seed)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    x = f32_to_bf16_bits(rng.standard_normal((b, k)))
+    mw, c_ref, s_ref = _quant_check(w, f"gemv {what}")
+    say(f"mxfp4_gemv n={n} k={k} b={b}")
+    y = host(bg.mxfp4_gemv(dev_bf16(x), mw))
+    assert_close(y, oracle.mx_matmul(x, c_ref, s_ref, n, k), f"mx y n={n} k={k} b={b}")
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (5, 384), (67, 2048 + 128), (300, 4096), (129, 11008), (33, 28672),
+                                 (16384 + 37, 2048 + 512), (8192 + 3, 16384 + 512)])
+def test_gemv_batch1(n, k):
+    """One to many chunks of 2048 k, partial last chunks, ragged rows, and
+    tall matrices (8 rows per wave)."""
+    _gemv_case(n, k, 1, seed=n % 97)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 8, 9, 16])
+def test_gemv_batches(b):
+    _gemv_case(203, 4096 + 640, b, seed=b)
+
+
+def test_gemv_batch_over_16_is_unsupported():
+    import torch
+    mw = bg.mxfp4_quantize(torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(bg.LibquantError) as e:
+        bg.mxfp4_gemv(torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda"), mw)
+    assert e.value.status == bg.LQ_ERR_UNSUPPORTED
+
+
+def test_workload_gate_up_sampled_rows():
+    """The 70B-shaped gate|up matrix (57344 x 8192) at full size: sampled
+    rows of the codes and scales bit-exact, and the batch-1 outputs of those
+    rows against the oracle one by one."""
+    wl = WORKLOADS["llama70b_decode"]
+    import torch
+    w = torch.cat([dev_bf16(wl.weight(0, i)) for i in (4, 5)], 0)
+    n, k = w.shape
+    say(f"mxfp4 gate|up {n}x{k}")
+    mw = bg.mxfp4_quantize(w)
+    x = wl.activation(k, 1)
+    y = host(bg.mxfp4_gemv(dev_bf16(x), mw))
+    rows = np.sort(np.random.default_rng(1).choice(n, 48, replace=False))
+    wr = host(w[torch.from_numpy(rows).cuda()].view(torch.int16)).view(np.uint16)
+    c_ref, s_ref = oracle.mx_quantize(wr)
+    assert_same_bits(host(mw.codes)[rows], c_ref, "sampled codes")
+    assert_same_bits(host(mw.scales)[rows], s_ref, "sampled scales")
+    assert_close(y[:, rows], oracle.mx_matmul(x, c_ref, s_ref, rows.size, k), "sampled y")
