@@ -167,6 +167,52 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
     del packed8
     torch.cuda.empty_cache()
 
+    # f4: MXFP4 weights (E2M1 + E8M0 per 32), the same 70B stack: quantize
+    # every layer, then a whole token per replay at batch 1, 4 and 16
+    n_sets = min(wl.distinct_layers, 2)
+    src = []
+    for s_ in range(n_sets):
+        mats = []
+        for g in groups:
+            parts = [dev_bf16(wl.weight(s_, i)) for i in g]
+            mats.append(torch.cat(parts, 0) if len(parts) > 1 else parts[0])
+            del parts
+        src.append(mats)
+    mq = [bg.mxfp4_quantize(m) for m in src[0]]
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    packed_mx = [[bg.mxfp4_quantize(m) for m in src[layer % n_sets]] for layer in range(wl.layers)]
+    ev[1].record()
+    torch.cuda.synchronize()
+    mq_ms = ev[0].elapsed_time(ev[1])
+    mq_bytes = sum(n * k * 2 for n, k in shapes) * wl.layers + sum(p.nbytes() for lay in packed_mx for p in lay)
+    del src, mq
+    torch.cuda.empty_cache()
+    mx = {"quantize": {"ms": round(mq_ms, 3), "GBps": round(mq_bytes / (mq_ms * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(mq_bytes / (mq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    log(f"[bench] mxfp4_quantize {wl.name}: {mq_ms:.1f} ms, {mx['quantize']['GBps']} GB/s")
+    for b in (1, 4, 16):
+        xs = {k: dev_bf16(wl.activation(k, b)) for k in sorted({k for _, k in shapes})}
+        ys = [torch.empty((b, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+
+        def sweep_mx():
+            for layer in range(wl.layers):
+                for j, (n, k) in enumerate(shapes):
+                    bg.mxfp4_gemv(xs[k], packed_mx[layer][j], ys[j])
+
+        ms = _graph_ms(sweep_mx, reps=5)
+        byt = wl.layers * sum(n * k // 2 + n * k // 32 + b * k * 2 + b * n * 4 for n, k in shapes)
+        tbs = byt / (ms * 1e-3) / 1e12
+        mx[f"batch{b}"] = {"ms_per_token_step": round(ms, 4), "TBps": round(tbs, 4),
+                           "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4), "bytes": byt}
+        log(f"[bench] mxfp4_gemv {wl.name} batch {b}: {ms:.3f} ms/step, {tbs:.3f} TB/s")
+        del xs, ys
+    rows["mxfp4_decode"] = {"workload": wl.name, "layers": wl.layers, "bound": "hbm",
+                            "quant": "MXFP4 (E2M1, E8M0 scale per 32)", **mx}
+    del packed_mx
+    torch.cuda.empty_cache()
+
     # f1: AWQ scale search over the Llama-2-7B layer, 512 calibration tokens
     aw = WORKLOADS["awq7b"]
     n_grid = aw.extra["n_grid"]

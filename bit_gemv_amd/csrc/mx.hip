@@ -121,17 +121,23 @@ __global__ __launch_bounds__(256) void mx_gemv_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int r = 0; r < RW; ++r) acc[b][r] = 0.0f;
 
+    // batch rows are taken BP at a time: a lane's 32 activations of one batch
+    // row are 16 registers, so all 16 rows at once would not fit with the codes
+    constexpr int BP = B < 4 ? B : 4;
     for (int c = ks; c < nchunks; c += ks_count) {
         const int k0 = c * kMxChunk + lane * 32;
         const bool kv = k0 < k;
-        u32x4 xv[B][4];
+        const uint32_t xo = kv ? (uint32_t)k0 * 2 : kOutOfRange;
+        auto load_x = [&](int b0, u32x4 (&xv)[BP][4]) {
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const auto rx = make_rsrc(x + (int64_t)b * k, b < bsz ? (uint32_t)k * 2 : 0u);
-            const uint32_t xo = kv ? (uint32_t)k0 * 2 : kOutOfRange;
+            for (int b = 0; b < BP; ++b) {
+                const auto rx = make_rsrc(x + (int64_t)(b0 + b) * k, b0 + b < bsz ? (uint32_t)k * 2 : 0u);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * j, 0, 0);
-        }
+                for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16 * j, 0, 0);
+            }
+        };
+        u32x4 xv[BP][4];
+        load_x(0, xv);
         const uint32_t co = kv ? (uint32_t)k0 / 2 : kOutOfRange;
         u32x4 cw[RW];
 #pragma unroll
@@ -156,27 +162,35 @@ __global__ __launch_bounds__(256) void mx_gemv_kernel(const uint16_t *__restrict
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const uint32_t cwv[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-            uint32_t p[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                p[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 0));
-                p[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 1));
-                p[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 2));
-                p[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 3));
+        for (int b0 = 0; b0 < B; b0 += BP) {
+            if (b0 > 0) {
+                // keep the next rows' loads (and registers) out of the previous pass
+                __builtin_amdgcn_sched_barrier(0);
+                load_x(b0, xv);
             }
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float d = 0.0f;
+            for (int r = 0; r < RW; ++r) {
+                const uint32_t cwv[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+                uint32_t p[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    d = dot2_bf16(p[4 * j + 0], xv[b][j].x, d);
-                    d = dot2_bf16(p[4 * j + 1], xv[b][j].y, d);
-                    d = dot2_bf16(p[4 * j + 2], xv[b][j].z, d);
-                    d = dot2_bf16(p[4 * j + 3], xv[b][j].w, d);
+                for (int q = 0; q < 4; ++q) {
+                    p[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 0));
+                    p[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 1));
+                    p[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 2));
+                    p[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwv[q], 1.0f, 3));
                 }
-                acc[b][r] = __builtin_fmaf(d, sc[r], acc[b][r]);
+#pragma unroll
+                for (int b = 0; b < BP; ++b) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        d = dot2_bf16(p[4 * j + 0], xv[b][j].x, d);
+                        d = dot2_bf16(p[4 * j + 1], xv[b][j].y, d);
+                        d = dot2_bf16(p[4 * j + 2], xv[b][j].z, d);
+                        d = dot2_bf16(p[4 * j + 3], xv[b][j].w, d);
+                    }
+                    acc[b0 + b][r] = __builtin_fmaf(d, sc[r], acc[b0 + b][r]);
+                }
             }
         }
     }
@@ -207,13 +221,13 @@ hipError_t launch_mx_rw(const MxArgs &a, hipStream_t st, int ks_count) {
 
 // Launch shape as the INT4 kernel (same code bytes per chunk): k split 4
 // ways at 4..7 chunks a row, 2 ways at 2..3 or 8 and more; 8 rows a wave
-// while that leaves 512 blocks and the batch allows it.
+// (batch up to 4) while that leaves 512 blocks.
 template <int B>
 hipError_t launch_mx(const MxArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kMxChunk - 1) / kMxChunk);
     const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
     const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
-    if constexpr (B <= 8) {
+    if constexpr (B <= 4) {  // 8 rows at larger batches would not fit the registers
         if (blocks8 >= 512) return launch_mx_rw<B, 8>(a, st, ks);
     }
     return launch_mx_rw<B, 4>(a, st, ks);
