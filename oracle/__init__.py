@@ -29,6 +29,11 @@ hold the pins):
   magnitude table and block size, exact round trips of representable
   blocks, constructed ties, brute-force nearest-value search, the scale
   rule at its boundaries, and numpy's matmul on the dequantized weights.
+* ``gptq_hessian`` / ``gptq_inverse_factor`` / ``gptq_quantize``: numpy's
+  2 X^T X and inverse, the reduction to plain RTN when H is a multiple of
+  the identity, an independent fp64 numpy implementation of the pages'
+  update formula with explicit inverses of the remaining submatrix, and the
+  pages' claim that the compensation lowers the output error versus RTN.
 * ``act_absmean`` / ``awq_scale`` / ``awq_loss`` / ``awq_search``: numpy
   recomputations of the channel means and of the output error from the
   pinned quantizer, the reduction to plain RTN at alpha = 0, and the pages'
@@ -85,6 +90,9 @@ def _load():
         lib.oracle_weight_only_matmul.argtypes = [P, I64, P, P, P, I64, I64, I, I, I64, P]
         lib.oracle_act_absmean.argtypes = [P, I64, I64, P]
         lib.oracle_mx_exponent.argtypes = [F]
+        lib.oracle_gptq_hessian.argtypes = [P, I64, I64, P]
+        lib.oracle_gptq_inverse_factor.argtypes = [P, I64, ctypes.c_double, P]
+        lib.oracle_gptq_quantize.argtypes = [P, I64, I64, P, I, I, I64, P, P, P]
         lib.oracle_mx_quantize.argtypes = [P, I64, I64, P, P]
         lib.oracle_mx_dequantize.argtypes = [P, P, I64, I64, P]
         lib.oracle_mx_matmul.argtypes = [P, I64, P, P, I64, I64, P]
@@ -329,3 +337,37 @@ def mx_matmul(x_bf16, codes, scales, n: int, k: int):
     _check(lib.oracle_mx_matmul(_ptr(x), m, _ptr(_c(codes, np.uint8)), _ptr(_c(scales, np.uint8)), n, k, _ptr(y)),
            "mx_matmul")
     return y
+
+
+def gptq_hessian(x_bf16):
+    """H = 2 X^T X in fp64; x: bf16 bits [t][k]."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    t, k = x.shape
+    h = np.zeros((k, k), np.float64)
+    _check(lib.oracle_gptq_hessian(_ptr(x), t, k, _ptr(h)), "gptq_hessian")
+    return h
+
+
+def gptq_inverse_factor(h, percdamp: float = 0.01):
+    """Damp H, then U (fp32, upper) with U^T U = H_damped^-1. Returns (H_damped, U)."""
+    lib = _load()
+    h = np.array(h, np.float64, copy=True, order="C")
+    k = h.shape[0]
+    u = np.zeros((k, k), np.float32)
+    _check(lib.oracle_gptq_inverse_factor(_ptr(h), k, float(percdamp), _ptr(u)), "gptq_inverse_factor")
+    return h, u
+
+
+def gptq_quantize(w_bf16, u, bits: int, symmetric: bool, group: int):
+    """The GPTQ column loop given U -> (codes, scales, zeros) as quantize() lays them out."""
+    lib = _load()
+    w = _c(w_bf16, np.uint16)
+    n, k = w.shape
+    ng = k // group
+    codes = np.zeros((n, k // 2 if bits == 4 else k), np.uint8)
+    scales = np.zeros((n, ng), np.float32)
+    zeros = None if symmetric else np.zeros((n, ng), np.float32)
+    _check(lib.oracle_gptq_quantize(_ptr(w), n, k, _ptr(_c(u, np.float32)), bits, int(bool(symmetric)), group,
+                                    _ptr(codes), _ptr(scales), _ptr(zeros)), "gptq_quantize")
+    return codes, scales, zeros

@@ -660,3 +660,128 @@ int oracle_mx_matmul(const uint16_t *x, int64_t m, const uint8_t *codes, const u
     free(mrow);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * GPTQ ([LP] "GPTQ: compensating the error just made"; [RL] GPTQ steps;
+ * [CP] GPTQ). Per layer, on calibration data X, minimise ||W X - W_hat X||^2
+ * by quantizing W column by column and, after column j (error
+ * e_j = w_j - quant(w_j)), moving the not yet quantized columns F:
+ *   W[:, F] -= e_j / [H^-1]_jj * [H^-1]_{j, F},   H = 2 X X^T,
+ * with the shared column order, lazy batched updates and the Cholesky form
+ * the pages name. In the Cholesky form, with U the upper Cholesky factor of
+ * H^-1 (U^T U = H^-1), the update of column j is
+ *   d = (w_j - w_hat_j) / U_jj,   w_f -= d * U_jf for every f > j.
+ * Readings (the pages leave these open):
+ *  - X is [t][k] (tokens x input channels), so H = 2 X^T X is [k][k];
+ *  - H is damped before inversion: H_ii += 0.01 * mean_i(H_ii) (H is singular
+ *    when t < k; the pages give no damping value);
+ *  - U is computed from the reverse Cholesky factor V of H (H = V V^T, V upper)
+ *    as U = V^-1, in fp64, then rounded to fp32;
+ *  - the weights are updated in fp32, each column's update applied to every
+ *    later column as one fused multiply-add, in column order (the lazy
+ *    batches regroup these updates but keep their order);
+ *  - groups follow quantize_groupwise: a group's scale and zero are taken
+ *    from the current (already compensated) weights of the group when its
+ *    first column is reached; codes round as RTN does.
+ * ---------------------------------------------------------------------- */
+
+/* H = 2 X^T X in fp64 (products of bf16 values are exact). x: [t][k]. */
+int oracle_gptq_hessian(const uint16_t *x, int64_t t, int64_t k, double *h)
+{
+    if (t <= 0 || k <= 0) return -1;
+    for (int64_t i = 0; i < k; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < t; ++r)
+                acc += (double)bf16_bits_to_f32(x[r * k + i]) * (double)bf16_bits_to_f32(x[r * k + j]);
+            h[i * k + j] = h[j * k + i] = 2.0 * acc;
+        }
+    return 0;
+}
+
+/* Damping (percdamp of the mean diagonal added to the diagonal), then U:
+ * V upper with H = V V^T (reverse Cholesky, last index first), U = V^-1.
+ * h is overwritten by the damped H. u: fp32 [k][k], lower triangle zero.
+ * Returns -1 if H is not positive definite after damping. */
+int oracle_gptq_inverse_factor(double *h, int64_t k, double percdamp, float *u)
+{
+    if (k <= 0) return -1;
+    double mean = 0.0;
+    for (int64_t i = 0; i < k; ++i) mean += h[i * k + i];
+    mean /= (double)k;
+    for (int64_t i = 0; i < k; ++i) h[i * k + i] += percdamp * mean;
+    double *v = (double *)calloc((size_t)(k * k), sizeof(double));
+    double *w = (double *)calloc((size_t)(k * k), sizeof(double));
+    int rc = -1;
+    if (!v || !w) goto out;
+    /* reverse Cholesky: for j = k-1 .. 0, using the columns right of j */
+    for (int64_t j = k - 1; j >= 0; --j) {
+        double d = h[j * k + j];
+        for (int64_t c = j + 1; c < k; ++c) d -= v[j * k + c] * v[j * k + c];
+        if (!(d > 0.0)) goto out;
+        const double vjj = sqrt(d);
+        v[j * k + j] = vjj;
+        for (int64_t i = 0; i < j; ++i) {
+            double s = h[i * k + j];
+            for (int64_t c = j + 1; c < k; ++c) s -= v[i * k + c] * v[j * k + c];
+            v[i * k + j] = s / vjj;
+        }
+    }
+    /* W = V^-1 (upper): back substitution, column by column */
+    for (int64_t c = 0; c < k; ++c) {
+        w[c * k + c] = 1.0 / v[c * k + c];
+        for (int64_t i = c - 1; i >= 0; --i) {
+            double s = 0.0;
+            for (int64_t m = i + 1; m <= c; ++m) s += v[i * k + m] * w[m * k + c];
+            w[i * k + c] = -s / v[i * k + i];
+        }
+    }
+    for (int64_t i = 0; i < k * k; ++i) u[i] = (float)w[i];
+    rc = 0;
+out:
+    free(v);
+    free(w);
+    return rc;
+}
+
+/* The column loop, given U (fp32 [k][k], upper). w: bf16 [n][k]; outputs as
+ * oracle_quantize_f32. Rows are independent. */
+int oracle_gptq_quantize(const uint16_t *w, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                         int64_t group, uint8_t *codes, float *scales, float *zeros)
+{
+    if (check_args(n, k, bits, group)) return -1;
+    const int64_t ng = k / group;
+    const int64_t row_bytes = bits == 4 ? k / 2 : k;
+    float *row = (float *)malloc(sizeof(float) * (size_t)k);
+    int32_t *q = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    int32_t *qg = (int32_t *)malloc(sizeof(int32_t) * (size_t)group);
+    if (!row || !q || !qg) { free(row); free(q); free(qg); return -1; }
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t j = 0; j < k; ++j) row[j] = bf16_bits_to_f32(w[r * k + j]);
+        float s = 1.0f, z = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            if (j % group == 0) {
+                /* this group's scale and zero from its current weights */
+                quantize_group(row + j, group, bits, symmetric, qg, &s, &z);
+                scales[r * ng + j / group] = s;
+                if (!symmetric) zeros[r * ng + j / group] = z;
+            }
+            /* the code of column j: the RTN formulas with the group's s, z */
+            float qf;
+            if (symmetric) {
+                const float qmax = (float)((1 << (bits - 1)) - 1);
+                qf = clampf(rintf(row[j] / s), -qmax, qmax);
+            } else {
+                const float qmaxu = (float)((1 << bits) - 1);
+                qf = clampf(rintf(row[j] / s) + z, 0.0f, qmaxu);
+            }
+            q[j] = (int32_t)qf;
+            const float w_hat = (qf - z) * s;
+            const float d = (row[j] - w_hat) / u[j * k + j];
+            for (int64_t f = j + 1; f < k; ++f) row[f] = fmaf(-d, u[j * k + f], row[f]);
+        }
+        store_codes(q, k, bits, symmetric, codes + r * row_bytes);
+    }
+    free(row); free(q); free(qg);
+    return 0;
+}

@@ -55,6 +55,14 @@ MUTANTS = {
                         "codes[r * (k / 2) + b * 16 + j / 2] = (uint8_t)(nib[j + 1] | (nib[j] << 4));"),
     "mx_negative_zero_kept": ("nib[j] = (uint8_t)(mag == 0 ? 0 : ((v < 0.0f ? 8 : 0) | mag));",
                               "nib[j] = (uint8_t)((v < 0.0f ? 8 : 0) | mag);"),
+    "gptq_update_sign": ("for (int64_t f = j + 1; f < k; ++f) row[f] = fmaf(-d, u[j * k + f], row[f]);",
+                         "for (int64_t f = j + 1; f < k; ++f) row[f] = fmaf(d, u[j * k + f], row[f]);"),
+    "gptq_error_not_scaled": ("const float d = (row[j] - w_hat) / u[j * k + j];", "const float d = (row[j] - w_hat);"),
+    "gptq_updates_stay_in_group": ("for (int64_t f = j + 1; f < k; ++f) row[f] = fmaf(-d, u[j * k + f], row[f]);",
+                                   "for (int64_t f = j + 1; f < (j / group + 1) * group; ++f) row[f] = fmaf(-d, u[j * k + f], row[f]);"),
+    "gptq_absolute_damping": ("for (int64_t i = 0; i < k; ++i) h[i * k + i] += percdamp * mean;",
+                              "for (int64_t i = 0; i < k; ++i) h[i * k + i] += percdamp;"),
+    "gptq_hessian_without_2": ("h[i * k + j] = h[j * k + i] = 2.0 * acc;", "h[i * k + j] = h[j * k + i] = acc;"),
     "smooth_inverted": ("s[j] = sqrtf(a) / sqrtf(b);", "s[j] = sqrtf(b) / sqrtf(a);"),
     "smooth_alpha_swapped": ("s[j] = powf(a, alpha) / powf(b, 1.0f - alpha);",
                              "s[j] = powf(a, 1.0f - alpha) / powf(b, alpha);"),

@@ -709,3 +709,112 @@ def test_mx_matmul_is_x_times_dequantized_transpose():
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
     full = bf16_bits_to_f32(x).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
     assert np.linalg.norm(y - full) / np.linalg.norm(full) < 0.2
+
+
+# --------------------------------------------------------------------------
+# GPTQ ("3.6 Quantization", GPTQ section).
+# --------------------------------------------------------------------------
+def _gptq_case(seed, t, n, k, corr=0.9):
+    """Calibration X with correlated channels (a random mixing matrix), so
+    that H is far from diagonal and compensation has something to do."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((t, k))
+    mix = np.eye(k) + corr * rng.standard_normal((k, k)) / np.sqrt(k)
+    x = f32_to_bf16_bits(base @ mix)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    return x, w
+
+
+def test_gptq_hessian_is_two_xtx():
+    from workloads import bf16_bits_to_f32
+    x, _ = _gptq_case(50, 24, 4, 128)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    assert np.allclose(oracle.gptq_hessian(x), 2 * xf.T @ xf, rtol=1e-13, atol=1e-12)
+
+
+def test_gptq_inverse_factor_is_the_cholesky_factor_of_the_inverse():
+    """U is upper triangular with U^T U = (damped H)^-1; the damping adds 1 %
+    of the mean diagonal (H of 24 tokens over 128 channels is singular)."""
+    x, _ = _gptq_case(51, 24, 4, 128)
+    h = oracle.gptq_hessian(x)
+    hd, u = oracle.gptq_inverse_factor(h, 0.01)
+    assert np.allclose(np.diag(hd) - np.diag(h), 0.01 * np.mean(np.diag(h)), rtol=1e-12)
+    assert np.all(np.tril(u, -1) == 0) and np.all(np.diag(u) > 0)
+    inv = np.linalg.inv(hd)
+    ud = u.astype(np.float64)
+    assert np.linalg.norm(ud.T @ ud - inv) / np.linalg.norm(inv) < 1e-5
+    # and it is the Cholesky factor (unique with a positive diagonal)
+    assert np.allclose(ud, np.linalg.cholesky(inv).T, rtol=1e-4, atol=1e-6 * np.abs(ud).max())
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_gptq_with_a_multiple_of_the_identity_is_plain_rtn(symmetric):
+    """H = c I makes U diagonal, so no column moves another: the codes are
+    exactly the RTN codes of the original weights."""
+    _, w = _gptq_case(52, 8, 6, 256)
+    _, u = oracle.gptq_inverse_factor(3.0 * np.eye(256), 0.01)
+    got = oracle.gptq_quantize(w, u, 4, symmetric, 128)
+    want = oracle.quantize(w, 4, symmetric, 128)
+    for g, r in zip(got, want):
+        if r is not None:
+            assert np.array_equal(g, r)
+
+
+def _gptq_numpy(w_f32, hd, bits, symmetric, group):
+    """The pages' update with explicit inverses of the remaining submatrix, in
+    fp64: W_F -= e_j / [H_F^-1]_jj [H_F^-1]_{j,F}, then H_F^-1 loses row and
+    column j (the block-inverse downdate). Returns the codes per column."""
+    n, k = w_f32.shape
+    qmax = 2 ** (bits - 1) - 1
+    qmaxu = 2 ** bits - 1
+    codes = np.zeros((n, k), np.int64)
+    for r in range(n):
+        w = w_f32[r].astype(np.float64)
+        hinv = np.linalg.inv(hd)
+        for j in range(k):
+            if j % group == 0:
+                g = w[j:j + group].astype(np.float32).astype(np.float64)
+                if symmetric:
+                    s = max(np.abs(g).max(), 1e-8) / qmax
+                    z = 0.0
+                else:
+                    mn, mx = g.min(), g.max()
+                    s = max(mx - mn, 1e-8) / qmaxu
+                    z = np.round(-mn / s)
+            q = np.clip(np.round(w[j] / s), -qmax, qmax) if symmetric else np.clip(np.round(w[j] / s) + z, 0, qmaxu)
+            codes[r, j] = q
+            e = w[j] - (q - z) * s
+            w[j + 1:] -= e / hinv[j, j] * hinv[j, j + 1:]
+            hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
+    return codes
+
+
+def test_gptq_matches_the_explicit_inverse_formula():
+    """The Cholesky-form fp32 oracle against the pages' formula in fp64:
+    near-ties aside (fp32 vs fp64 sums), the codes are the same."""
+    from workloads import bf16_bits_to_f32
+    x, w = _gptq_case(53, 64, 6, 256)
+    hd, u = oracle.gptq_inverse_factor(oracle.gptq_hessian(x), 0.01)
+    codes, _, _ = oracle.gptq_quantize(w, u, 4, False, 128)
+    got = _unpack4(codes, 256)
+    want = _gptq_numpy(bf16_bits_to_f32(w), hd, 4, False, 128)
+    assert np.mean(got == want) >= 0.995
+
+
+def test_gptq_lowers_the_output_error_against_rtn():
+    """The GPTQ section's claim: compensating each rounding error in the
+    columns not yet quantized lowers ||W X - W_hat X|| on the calibration
+    data against rounding every weight on its own."""
+    from workloads import bf16_bits_to_f32
+    x, w = _gptq_case(54, 96, 16, 256)
+    n, k = 16, 256
+    hd, u = oracle.gptq_inverse_factor(oracle.gptq_hessian(x), 0.01)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    wf = bf16_bits_to_f32(w).astype(np.float64)
+    def out_err(c, s, z):
+        w_hat = oracle.dequantize(c, s, z, n, k, 4, False, 128).astype(np.float64)
+        return np.linalg.norm(xf @ (wf - w_hat).T)
+    e_gptq = out_err(*oracle.gptq_quantize(w, u, 4, False, 128))
+    e_rtn = out_err(*oracle.quantize(w, 4, False, 128))
+    assert e_gptq < 0.8 * e_rtn
