@@ -769,11 +769,11 @@ int oracle_gptq_quantize(const uint16_t *w, int64_t n, int64_t k, const float *u
             /* the code of column j: the RTN formulas with the group's s, z */
             float qf;
             if (symmetric) {
-                const float qmax = (float)((1 << (bits - 1)) - 1);
-                qf = clampf(rintf(row[j] / s), -qmax, qmax);
+                const float top = (float)((1 << (bits - 1)) - 1); /* 7 or 127 */
+                qf = clampf(rintf(row[j] / s), -top, top);
             } else {
-                const float qmaxu = (float)((1 << bits) - 1);
-                qf = clampf(rintf(row[j] / s) + z, 0.0f, qmaxu);
+                const float top = (float)((1 << bits) - 1);       /* 15 or 255 */
+                qf = clampf(rintf(row[j] / s) + z, 0.0f, top);
             }
             q[j] = (int32_t)qf;
             const float w_hat = (qf - z) * s;
