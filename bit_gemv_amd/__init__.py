@@ -27,7 +27,7 @@ LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = ra
 
 ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w8a16_gemv", "w4a16_gemm",
                 "smooth_scale", "quant_per_token_int8", "w8a8_gemm", "act_absmean", "awq_search",
-                "mxfp4_quantize", "mxfp4_gemv")
+                "mxfp4_quantize", "mxfp4_gemv", "gptq_hessian_factor", "gptq_quantize")
 
 
 class LibquantError(RuntimeError):
@@ -62,6 +62,8 @@ def load_library(path: Optional[str] = None):
         "act_absmean": [P, I64, I64, P, P],
         "mxfp4_quantize": [P, I64, I64, P, P, P],
         "mxfp4_gemv": [P, I64, P, P, I64, I64, P, P],
+        "gptq_hessian_factor": [P, I64, I64, F, P, I64, P, P],
+        "gptq_quantize": [P, I64, I64, P, I, I, I64, P, I64, P, P, P, P],
         "awq_search": [P, I64, P, I64, I64, I, I64, I, P, P, I64, P, P, P, P, P, P, P],
     }
     for name, argtypes in sigs.items():
@@ -75,6 +77,8 @@ def load_library(path: Optional[str] = None):
     lib.lq_abi_version.restype = ctypes.c_int
     lib.awq_workspace_bytes.argtypes = [I64, I64, I64]
     lib.awq_workspace_bytes.restype = ctypes.c_int64
+    lib.gptq_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.gptq_workspace_bytes.restype = ctypes.c_int64
     if path is None:
         _lib = lib
     return lib
@@ -337,3 +341,44 @@ def mxfp4_gemv(x: torch.Tensor, mw: MxWeight, y: Optional[torch.Tensor] = None) 
     _need(y, "y", torch.float32, (m, mw.n))
     _call("mxfp4_gemv", _ptr(x), m, _ptr(mw.codes), _ptr(mw.scales), mw.n, mw.k, _ptr(y), _stream())
     return y
+
+
+def _gptq_workspace(t: int, n: int, k: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    need = load_library().gptq_workspace_bytes(t, n, k)
+    if need < 0:
+        raise LibquantError(LQ_ERR_INVALID_ARG, "gptq", "sizes out of range")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", torch.uint8)
+    return workspace
+
+
+def gptq_hessian_factor(x: torch.Tensor, percdamp: float = 0.01, u: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """U (fp32 [k][k], upper) with U^T U = (2 X^T X + damping)^-1, X [t][k] bf16."""
+    _need(x, "x", torch.bfloat16)
+    t, k = x.shape
+    if u is None:
+        u = torch.empty((k, k), dtype=torch.float32, device=x.device)
+    _need(u, "u", torch.float32, (k, k))
+    ws = _gptq_workspace(t, 0, k, x.device, workspace)
+    _call("gptq_hessian_factor", _ptr(x), t, k, float(percdamp), _ptr(ws), ws.numel(), _ptr(u), _stream())
+    return u
+
+
+def gptq_quantize(w: torch.Tensor, u: torch.Tensor, bits: int = 4, symmetric: bool = False, group: int = 128,
+                  workspace: Optional[torch.Tensor] = None) -> PackedWeight:
+    """GPTQ's column loop on bf16 W[n][k] with the factor U -> a PackedWeight
+    laid out as quantize_groupwise's."""
+    _need(w, "w", torch.bfloat16)
+    n, k = w.shape
+    _need(u, "u", torch.float32, (k, k))
+    dev = w.device
+    ng = k // group if group > 0 and k % group == 0 else 0
+    codes = torch.empty((n, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, ng), dtype=torch.float32, device=dev)
+    zeros = None if symmetric else torch.empty((n, ng), dtype=torch.float32, device=dev)
+    ws = _gptq_workspace(0, n, k, dev, workspace)
+    _call("gptq_quantize", _ptr(w), n, k, _ptr(u), bits, int(bool(symmetric)), group, _ptr(ws), ws.numel(),
+          _ptr(codes), _ptr(scales), _ptr(zeros), _stream())
+    return PackedWeight(codes, scales, zeros, n, k, bits, bool(symmetric), group)

@@ -326,6 +326,70 @@ lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const voi
     return launched(lq::launch_mx_gemv(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int64_t gptq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
+    if (t < 0 || n < 0 || k <= 0 || t > kMaxDim || n > kMaxDim || k > kMaxDim || k * k > kMaxElems ||
+        n * k > kMaxElems || t * k > kMaxElems)
+        return -1;
+    const int64_t f = t > 0 ? lq::gptq_factor_workspace_bytes(t, k) : 0;
+    const int64_t q = n > 0 ? lq::gptq_quantize_workspace_bytes(n, k) : 0;
+    return f > q ? f : q;
+}
+
+lq_status gptq_hessian_factor(const void *x_bf16, int64_t t, int64_t k, float percdamp, void *workspace,
+                              int64_t workspace_bytes, float *u, void *stream) {
+    const char *fn = "gptq_hessian_factor";
+    if (t <= 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t and k must be positive", fn);
+    if (!(percdamp > 0.0f && percdamp <= 1.0f)) return fail(LQ_ERR_INVALID_ARG, "%s: percdamp must be in (0, 1]", fn);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (t > kMaxDim || k > 65536 || t * k > kMaxElems || t >= (int64_t(1) << 24))
+        return fail(LQ_ERR_UNSUPPORTED, "%s: t or k too large", fn);
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!u || !aligned(u, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: u null or not 16-byte aligned", fn);
+    const int64_t need = lq::gptq_factor_workspace_bytes(t, k);
+    if (!workspace || !aligned(workspace, 256))
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+    if (workspace_bytes < need)
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                    (long long)need);
+    if (any_overlap({{u, k * k * 4}, {workspace, need}}, {{x_bf16, t * k * 2}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: u or the workspace overlaps x or each other", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    return launched(lq::launch_gptq_factor(static_cast<const uint16_t *>(x_bf16), t, k, percdamp, workspace, u,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                        int64_t group, void *workspace, int64_t workspace_bytes, void *codes, float *scales,
+                        float *zeros, void *stream) {
+    const char *fn = "gptq_quantize";
+    if (n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative n", fn);
+    lq_status st = check_group(fn, k, bits, group);
+    if (st != LQ_OK) return st;
+    if (n > kMaxDim || k > 65536 || n * k > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: matrix too large", fn);
+    if (n == 0) return LQ_OK;
+    if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
+    if (!u || !aligned(u, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: u null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if ((st = check_meta(fn, symmetric, scales, zeros)) != LQ_OK) return st;
+    const int64_t need = lq::gptq_quantize_workspace_bytes(n, k);
+    if (!workspace || !aligned(workspace, 256))
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+    if (workspace_bytes < need)
+        return fail(LQ_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                    (long long)need);
+    const int64_t meta = n * (k / group) * 4;
+    const int64_t cbytes = bits == 4 ? n * k / 2 : n * k;
+    if (any_overlap({{workspace, need}, {codes, cbytes}, {scales, meta}, {zeros, symmetric ? 0 : meta}},
+                    {{w_bf16, n * k * 2}, {u, k * k * 4}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output or the workspace overlaps an input or another output", fn);
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::GptqArgs a{static_cast<const uint16_t *>(w_bf16), n, k, u, bits, symmetric, group, workspace,
+                   static_cast<uint8_t *>(codes), scales, zeros};
+    return launched(lq::launch_gptq_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 lq_status act_absmean(const void *x_bf16, int64_t t, int64_t k, float *sx, void *stream) {
     const char *fn = "act_absmean";
     if (t <= 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: t and k must be positive (a mean of no tokens)", fn);

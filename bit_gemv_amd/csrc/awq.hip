@@ -283,6 +283,13 @@ constexpr int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
+hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int64_t n, int64_t k, float *y,
+                            hipStream_t st) {
+    const uint32_t blocks = (uint32_t)(((n + GB_N - 1) / GB_N) * ((m + GB_M - 1) / GB_M));
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(blocks), dim3(256), 0, st, a, b, (int)m, (int)n, (int)k, y);
+    return hipGetLastError();
+}
+
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
     return 2 * align256(t * n * 4) + align256(t * k * 2) + align256(k * 4) + align256(kSqBlocks * 8);
 }
@@ -305,10 +312,7 @@ hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st) {
     double *partials = reinterpret_cast<double *>(ws);
 
     hipError_t e;
-    const uint32_t gb_blocks = (uint32_t)(((a.n + GB_N - 1) / GB_N) * ((a.t + GB_M - 1) / GB_M));
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(gb_blocks), dim3(256), 0, st, a.x, a.w, (int)a.t, (int)a.n, (int)a.k,
-                       y_ref);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(a.x, a.w, a.t, a.n, a.k, y_ref, st)) != hipSuccess) return e;
 
     const uint32_t kblocks = (uint32_t)((a.k + 255) / 256);
     const int64_t x8 = a.t * a.k / 8;

@@ -1,0 +1,407 @@
+// gptq.hip -- GPTQ error-compensated rounding on gfx950.
+//
+// Method ("3.6 Quantization", GPTQ section; "LLM quantization deep dive" and
+// the PTQ concept page, GPTQ): per layer, minimise ||W X - W_hat X||^2 on
+// calibration data by quantizing W one input column at a time and moving
+// the columns not yet quantized to absorb each rounding error,
+//   W[:, F] -= e_j / [H^-1]_jj [H^-1]_{j, F},   H = 2 X X^T,
+// with one column order for all rows, lazily batched updates and the
+// Cholesky form. With U the upper Cholesky factor of H^-1 (U^T U = H^-1) the
+// step for column j is d = (w_j - w_hat_j) / U_jj, w_f -= d U_jf for f > j.
+// Readings where the pages leave a step open: X is [t][k] (tokens x input
+// channels); H is damped by 1 % of its mean diagonal (it is singular when
+// t < k); U = V^-1 for the reverse Cholesky factor V of H (H = V V^T, V
+// upper); weights are updated in fp32, each column's update applied to
+// every later column as one fused multiply-add, in column order; a group's
+// scale and zero come from its current (compensated) weights when its first
+// column is reached, and codes round as the RTN quantizer does.
+//
+// Two entry points:
+//  * the factor: X^T (bf16, zero-padded to 64 tokens) -> H = X^T X on bf16
+//    MFMA -> 2 H + damping -> blocked reverse Cholesky in 64-wide panels
+//    (the panel's diagonal block factored and inverted by one workgroup in
+//    LDS, panel and trailing updates by an fp32 GEMM) -> blocked inverse of
+//    V -> U, all fp32;
+//  * the column loop: per 128-column block, one wave per row walks the
+//    block's columns with the block of U in LDS (the codes, the group's
+//    scale and zero, the scaled errors d); then the later columns take the
+//    block's updates as one fp32 GEMM, W[:, F] = W[:, F] - D U[block, F],
+//    whose accumulator starts at W and adds the block's terms in column
+//    order with fused multiply-adds -- the same operations, in the same
+//    order, as applying each column's update as it is made.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lq {
+
+namespace {
+
+// --------------------------------------------------------------------------
+// fp32 GEMM: C[M][N] = (beta ? C : 0) + sgn * A[M][K] op(B), op(B) = B[K][N]
+// (BT = false) or B^T with B given [N][K] (BT = true). Each output is
+// accumulated in ascending K order with fused multiply-adds onto its start
+// value (sgn is +-1, so sgn * a is exact). 64 x 64 tiles, 256 threads of 4 x 4.
+// --------------------------------------------------------------------------
+template <bool BT>
+// (No __restrict__: the panel step computes V_AB in place over H_AB; each
+// workgroup reads all of its A rows before it writes the same rows of C.)
+__global__ __launch_bounds__(256) void sgemm_kernel(int M, int N, int K, float sgn, const float *A, int64_t lda,
+                                                    const float *B, int64_t ldb, int beta, float *C, int64_t ldc) {
+    __shared__ float As[16][68];
+    __shared__ float Bs[16][68];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
+            acc[r][c] = beta && i < M && j < N ? C[(int64_t)i * ldc + j] : 0.0f;
+        }
+    for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            {
+                const int row = e >> 4, kk = e & 15;  // A: 64 rows x 16 k
+                const int i = i0 + row, kg = k0 + kk;
+                As[kk][row] = i < M && kg < K ? A[(int64_t)i * lda + kg] : 0.0f;
+            }
+            if (BT) {
+                const int col = e >> 4, kk = e & 15;  // B^T: 64 rows (n) x 16 k
+                const int j = j0 + col, kg = k0 + kk;
+                Bs[kk][col] = j < N && kg < K ? B[(int64_t)j * ldb + kg] : 0.0f;
+            } else {
+                const int kk = e >> 6, col = e & 63;  // B: 16 k x 64 columns
+                const int j = j0 + col, kg = k0 + kk;
+                Bs[kk][col] = j < N && kg < K ? B[(int64_t)kg * ldb + j] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = sgn * As[kk][4 * ty + r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = Bs[kk][4 * tx + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
+            if (i < M && j < N) C[(int64_t)i * ldc + j] = acc[r][c];
+        }
+}
+
+template <bool BT>
+hipError_t sgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B, int64_t ldb,
+                 int beta, float *C, int64_t ldc, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((uint32_t)((N + 63) / 64), (uint32_t)((M + 63) / 64));
+    hipLaunchKernelGGL((sgemm_kernel<BT>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn, A, lda, B, ldb, beta,
+                       C, ldc);
+    return hipGetLastError();
+}
+
+// X [t][k] bf16 -> X^T [k][tp] bf16, tokens t .. tp - 1 zero (tp a multiple of 64).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ x, int t, int k, int tp,
+                                                             uint16_t *__restrict__ xt) {
+    __shared__ uint16_t tile[32][33];
+    const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;  // c: channel, r: token
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    for (int yy = ty; yy < 32; yy += 8) {
+        const int r = r0 + yy, c = c0 + tx;
+        tile[yy][tx] = r < t && c < k ? x[(int64_t)r * k + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int yy = ty; yy < 32; yy += 8) {
+        const int c = c0 + yy, r = r0 + tx;
+        if (c < k && r < tp) xt[(int64_t)c * tp + r] = tile[tx][yy];
+    }
+}
+
+// H = 2 H, then H_ii += percdamp * mean(H_ii): the diagonal's sum in fp64 by
+// one workgroup, in a fixed order.
+__global__ __launch_bounds__(256) void damp_sum_kernel(const float *__restrict__ h, int k, double *__restrict__ sum) {
+    __shared__ double lds[256];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < k; i += 256) acc += 2.0 * (double)h[(int64_t)i * k + i];
+    lds[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) lds[threadIdx.x] += lds[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *sum = lds[0];
+}
+
+__global__ __launch_bounds__(256) void damp_apply_kernel(float *__restrict__ h, int k, float percdamp,
+                                                         const double *__restrict__ sum) {
+    const int64_t total = (int64_t)k * k;
+    const float lam = (float)((double)percdamp * (*sum / (double)k));
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e / k, j = e % k;
+        h[e] = 2.0f * h[e] + (i == j ? lam : 0.0f);
+    }
+}
+
+constexpr int NB = 64;  // panel width of the factorisation
+
+// The diagonal block B = [j0, j0 + 64) of the (updated) H: reverse Cholesky
+// V_BB (H_BB = V_BB V_BB^T, upper) written back into H's block, and its
+// inverse into vinv (64 x 64, zeros below the diagonal). One workgroup.
+__global__ __launch_bounds__(256) void chol_diag_kernel(float *__restrict__ h, int k, int j0,
+                                                        float *__restrict__ vinv) {
+    __shared__ float V[NB][NB + 1];
+    __shared__ float W[NB][NB + 1];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < NB * NB; e += 256) V[e / NB][e % NB] = h[(int64_t)(j0 + e / NB) * k + j0 + e % NB];
+    __syncthreads();
+    for (int j = NB - 1; j >= 0; --j) {
+        if (tid == 0) {
+            float d = V[j][j];
+            for (int c = j + 1; c < NB; ++c) d -= V[j][c] * V[j][c];
+            V[j][j] = sqrtf(d);  // not positive definite: NaN, which propagates to U
+        }
+        __syncthreads();
+        if (tid < j) {
+            float s = V[tid][j];
+            for (int c = j + 1; c < NB; ++c) s -= V[tid][c] * V[j][c];
+            V[tid][j] = s / V[j][j];
+        }
+        __syncthreads();
+    }
+    // W = V^-1 (upper): thread c solves column c by back substitution
+    if (tid < NB) {
+        const int c = tid;
+        for (int i = 0; i < NB; ++i) W[i][c] = 0.0f;
+        W[c][c] = 1.0f / V[c][c];
+        for (int i = c - 1; i >= 0; --i) {
+            float s = 0.0f;
+            for (int m = i + 1; m <= c; ++m) s += V[i][m] * W[m][c];
+            W[i][c] = -s / V[i][i];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int i = e / NB, c = e % NB;
+        if (i <= c) h[(int64_t)(j0 + i) * k + j0 + c] = V[i][c];
+        vinv[e] = i <= c ? W[i][c] : 0.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float *__restrict__ p, int64_t count) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256) p[e] = 0.0f;
+}
+
+// U[j0:j0+64][j0:j0+64] = vinv block
+__global__ __launch_bounds__(256) void put_block_kernel(const float *__restrict__ blk, float *__restrict__ u, int k,
+                                                        int j0) {
+    for (int e = threadIdx.x; e < NB * NB; e += 256) u[(int64_t)(j0 + e / NB) * k + j0 + e % NB] = blk[e];
+}
+
+__global__ __launch_bounds__(256) void bf16_to_f32_kernel(const uint16_t *__restrict__ w, int64_t count,
+                                                          float *__restrict__ out) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256)
+        out[e] = bf16_lo((uint32_t)w[e]);
+}
+
+// --------------------------------------------------------------------------
+// The column loop of one 128-column block. One wave per row, lane l holding
+// columns j0 + l and j0 + 64 + l of the compensated row; the block of U
+// (128 x 128) in LDS, shared by the workgroup's 16 rows.
+// --------------------------------------------------------------------------
+constexpr int GB = 128;  // columns per block (the lazy batch)
+
+LQ_DEVICE float clampf_def(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+template <int BITS, bool SYM>
+__global__ __launch_bounds__(1024) void gptq_block_kernel(float *__restrict__ w, int n, int k,
+                                                          const float *__restrict__ u, int j0, int group,
+                                                          float *__restrict__ dbuf, uint8_t *__restrict__ codes,
+                                                          float *__restrict__ scales, float *__restrict__ zeros) {
+    __shared__ float Us[GB][GB + 1];
+    for (int e = threadIdx.x; e < GB * GB; e += 1024)
+        Us[e / GB][e % GB] = u[(int64_t)(j0 + e / GB) * k + j0 + e % GB];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 16 + (threadIdx.x >> 6);
+    if (r >= n) return;  // no barrier follows
+    float *row = w + (int64_t)r * k;
+    float a = row[j0 + lane], b = row[j0 + 64 + lane];
+    const int ng = k / group;
+    const int g = j0 / group;
+    float s, z;
+    if (j0 % group == 0) {
+        // the group's scale and zero from its current weights (the RTN formulas)
+        float mn = fminf(a, b), mx = fmaxf(a, b), am = fmaxf(fabsf(a), fabsf(b));
+        for (int c = j0 + 128 + lane; c < j0 + group; c += 64) {
+            const float v = row[c];
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+            am = fmaxf(am, fabsf(v));
+        }
+        if (SYM) {
+            am = team_max<64>(am);
+            if (am < kFloor) am = kFloor;
+            s = am / (float)((1 << (BITS - 1)) - 1);
+            z = 0.0f;
+        } else {
+            mn = team_min<64>(mn);
+            mx = team_max<64>(mx);
+            float range = mx - mn;
+            if (range < kFloor) range = kFloor;
+            s = range / (float)((1 << BITS) - 1);
+            z = rintf(-mn / s) + 0.0f;
+        }
+        if (lane == 0) {
+            scales[(int64_t)r * ng + g] = s;
+            if (!SYM) zeros[(int64_t)r * ng + g] = z;
+        }
+    } else {
+        s = scales[(int64_t)r * ng + g];
+        z = SYM ? 0.0f : zeros[(int64_t)r * ng + g];
+    }
+    int qa = 0, qb = 0;
+    float da = 0.0f, db = 0.0f;
+    for (int j = 0; j < GB; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(j < 64 ? a : b), j & 63));
+        float qf;
+        if (SYM) {
+            const float top = (float)((1 << (BITS - 1)) - 1);
+            qf = clampf_def(rintf(wj / s), -top, top);
+        } else {
+            const float top = (float)((1 << BITS) - 1);
+            qf = clampf_def(rintf(wj / s) + z, 0.0f, top);
+        }
+        const float d = (wj - (qf - z) * s) / Us[j][j];
+        if (lane > j) a = __builtin_fmaf(-d, Us[j][lane], a);
+        if (64 + lane > j) b = __builtin_fmaf(-d, Us[j][64 + lane], b);
+        if (lane == (j & 63)) {
+            if (j < 64) {
+                qa = (int)qf;
+                da = d;
+            } else {
+                qb = (int)qf;
+                db = d;
+            }
+        }
+    }
+    dbuf[(int64_t)r * GB + lane] = da;
+    dbuf[(int64_t)r * GB + 64 + lane] = db;
+    if (BITS == 4) {
+        const int ua = SYM ? qa + 8 : qa, ub = SYM ? qb + 8 : qb;
+        // element 2i in the low nibble: lane 2i takes its odd neighbour's code
+        const int na = __shfl_xor(ua, 1), nb = __shfl_xor(ub, 1);
+        if ((lane & 1) == 0) {
+            uint8_t *cr = codes + (int64_t)r * (k / 2);
+            cr[(j0 + lane) / 2] = (uint8_t)((ua & 0xF) | ((na & 0xF) << 4));
+            cr[(j0 + 64 + lane) / 2] = (uint8_t)((ub & 0xF) | ((nb & 0xF) << 4));
+        }
+    } else {
+        uint8_t *cr = codes + (int64_t)r * k;
+        cr[j0 + lane] = (uint8_t)qa;
+        cr[j0 + 64 + lane] = (uint8_t)qb;
+    }
+}
+
+constexpr int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+int64_t gptq_factor_workspace_bytes(int64_t t, int64_t k) {
+    const int64_t tp = (t + 63) / 64 * 64;
+    return align256(k * tp * 2) + align256(k * k * 4) + align256(k * NB * 4) + align256(k * NB * 4) + 256;
+}
+
+int64_t gptq_quantize_workspace_bytes(int64_t n, int64_t k) { return align256(n * k * 4) + align256(n * GB * 4); }
+
+hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float percdamp, void *workspace, float *u,
+                              hipStream_t st) {
+    const int64_t tp = (t + 63) / 64 * 64;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint16_t *xt = reinterpret_cast<uint16_t *>(ws);
+    ws += align256(k * tp * 2);
+    float *h = reinterpret_cast<float *>(ws);
+    ws += align256(k * k * 4);
+    float *vinv = reinterpret_cast<float *>(ws);  // [k / 64][64][64]
+    ws += align256(k * NB * 4);
+    float *tmp = reinterpret_cast<float *>(ws);  // [k][64]
+    ws += align256(k * NB * 4);
+    double *dsum = reinterpret_cast<double *>(ws);
+    hipError_t e;
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((uint32_t)((k + 31) / 32), (uint32_t)(tp / 32)), dim3(256), 0, st,
+                       x, (int)t, (int)k, (int)tp, xt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(xt, xt, k, k, tp, h, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(damp_sum_kernel, dim3(1), dim3(256), 0, st, h, (int)k, dsum);
+    hipLaunchKernelGGL(damp_apply_kernel, dim3(2048), dim3(256), 0, st, h, (int)k, percdamp, dsum);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int panels = (int)(k / NB);
+    // reverse Cholesky, last panel first
+    for (int p = panels - 1; p >= 0; --p) {
+        const int64_t j0 = (int64_t)p * NB;
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, h, (int)k, (int)j0, vinv + p * NB * NB);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (j0 == 0) continue;
+        // V_AB = H_AB Vinv_BB^T (in place), then H_AA -= V_AB V_AB^T
+        if ((e = sgemm<true>(j0, NB, NB, 1.0f, h + j0, k, vinv + p * NB * NB, NB, 0, h + j0, k, st)) != hipSuccess)
+            return e;
+        if ((e = sgemm<true>(j0, j0, NB, -1.0f, h + j0, k, h + j0, k, 1, h, k, st)) != hipSuccess) return e;
+    }
+    // U = V^-1, first panel first: U_BB = Vinv_BB, U_AB = -U_AA (V_AB U_BB)
+    hipLaunchKernelGGL(fill_kernel, dim3(2048), dim3(256), 0, st, u, k * k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    for (int p = 0; p < panels; ++p) {
+        const int64_t j0 = (int64_t)p * NB;
+        hipLaunchKernelGGL(put_block_kernel, dim3(1), dim3(256), 0, st, vinv + p * NB * NB, u, (int)k, (int)j0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (j0 == 0) continue;
+        if ((e = sgemm<false>(j0, NB, NB, 1.0f, h + j0, k, u + j0 * k + j0, k, 0, tmp, NB, st)) != hipSuccess)
+            return e;
+        if ((e = sgemm<false>(j0, NB, j0, -1.0f, u, k, tmp, NB, 0, u + j0, k, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gptq_quantize(const GptqArgs &a, hipStream_t st) {
+    uint8_t *ws = static_cast<uint8_t *>(a.workspace);
+    float *wf = reinterpret_cast<float *>(ws);
+    ws += align256(a.n * a.k * 4);
+    float *dbuf = reinterpret_cast<float *>(ws);
+    hipError_t e;
+    hipLaunchKernelGGL(bf16_to_f32_kernel, dim3(4096), dim3(256), 0, st, a.w, a.n * a.k, wf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint32_t blocks = (uint32_t)((a.n + 15) / 16);
+    for (int64_t j0 = 0; j0 < a.k; j0 += GB) {
+#define LQ_GPTQ_BLOCK(BITS, S)                                                                                     \
+    hipLaunchKernelGGL((gptq_block_kernel<BITS, S>), dim3(blocks), dim3(1024), 0, st, wf, (int)a.n, (int)a.k, a.u, \
+                       (int)j0, (int)a.group, dbuf, a.codes, a.scales, a.zeros)
+        if (a.bits == 4 && a.symmetric) LQ_GPTQ_BLOCK(4, true);
+        else if (a.bits == 4) LQ_GPTQ_BLOCK(4, false);
+        else if (a.symmetric) LQ_GPTQ_BLOCK(8, true);
+        else LQ_GPTQ_BLOCK(8, false);
+#undef LQ_GPTQ_BLOCK
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t f0 = j0 + GB;
+        if (f0 < a.k) {
+            // W[:, f0:] = W[:, f0:] - D U[j0:j0+128, f0:], in column order per element
+            if ((e = sgemm<false>(a.n, a.k - f0, GB, -1.0f, dbuf, GB, a.u + j0 * a.k + f0, a.k, 1, wf + f0, a.k, st)) !=
+                hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace lq

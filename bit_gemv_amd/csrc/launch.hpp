@@ -75,6 +75,18 @@ struct MxArgs {
     float *y;
 };
 
+// GPTQ column loop: weights, the inverse-Hessian factor U and the outputs.
+struct GptqArgs {
+    const uint16_t *w;  // [n][k]
+    int64_t n, k;
+    const float *u;     // [k][k], upper
+    int bits, symmetric;
+    int64_t group;
+    void *workspace;
+    uint8_t *codes;
+    float *scales, *zeros;
+};
+
 // AWQ scale search (bits 4): inputs, the caller's workspace and outputs.
 struct AwqArgs {
     const uint16_t *x;  // calibration activations [t][k]
@@ -106,6 +118,14 @@ hipError_t launch_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *
 hipError_t launch_mx_gemv(const MxArgs &a, hipStream_t st);
 hipError_t launch_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx, hipStream_t st);
 hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st);
+int64_t gptq_factor_workspace_bytes(int64_t t, int64_t k);
+int64_t gptq_quantize_workspace_bytes(int64_t n, int64_t k);
+hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float percdamp, void *workspace, float *u,
+                              hipStream_t st);
+hipError_t launch_gptq_quantize(const GptqArgs &a, hipStream_t st);
+// Y[m][n] = A[m][k] B[n][k]^T, bf16 inputs (k a multiple of 64), fp32 out.
+hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int64_t n, int64_t k, float *y,
+                            hipStream_t st);
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
 
 }  // namespace lq

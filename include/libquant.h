@@ -248,6 +248,51 @@ lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const voi
                      int64_t n, int64_t k, float *y, void *stream);
 
 /*
+ * gptq_workspace_bytes -- device workspace gptq_hessian_factor (t tokens, k
+ * channels) and gptq_quantize (n rows, k columns) need; the larger of the
+ * two (pass t = 0 or n = 0 for one of them). -1 for sizes they would reject.
+ */
+int64_t gptq_workspace_bytes(int64_t t, int64_t n, int64_t k);
+
+/*
+ * gptq_hessian_factor -- the inverse-Hessian factor GPTQ compensates with
+ * ("3.6 Quantization", GPTQ section: H = 2 X X^T of the layer's calibration
+ * inputs, and the Cholesky form of its inverse):
+ *   H = 2 X^T X (X [t][k]: tokens x input channels; bf16 products, fp32 sums)
+ *   H_ii += percdamp * mean_i H_ii  (damping: H is singular when t < k)
+ *   u = V^-1 with H = V V^T, V upper triangular (the reverse Cholesky factor),
+ *       so u is upper triangular with u^T u = H^-1.
+ * x_bf16 [t][k] (16-byte aligned); u out fp32 [k][k] (16-byte aligned,
+ * zeros below the diagonal). percdamp in (0, 1]; k a multiple of 128 and at
+ * most 65536; t below 2^24. workspace: at least gptq_workspace_bytes(t, 0, k)
+ * bytes, 256-byte aligned, scratch. If H is not positive definite after
+ * damping (e.g. X all zero), u holds NaN. Layers sharing an input (q, k, v)
+ * share u.
+ */
+lq_status gptq_hessian_factor(const void *x_bf16, int64_t t, int64_t k, float percdamp, void *workspace,
+                              int64_t workspace_bytes, float *u, void *stream);
+
+/*
+ * gptq_quantize -- GPTQ's column loop ("3.6 Quantization", GPTQ section: quantize
+ * W one input column at a time in one order for all rows; after column j
+ * move the columns not yet quantized to absorb its rounding error, with
+ * lazily batched updates; "LLM quantization deep dive", GPTQ steps):
+ *   for j = 0 .. k-1, per row:
+ *     at a group's first column: s, z from the group's current weights
+ *       (the quantize_groupwise formulas);
+ *     q_j = the quantize_groupwise code of w_j; d = (w_j - (q_j - z) s) / u_jj;
+ *     w_f = fma(-d, u_jf, w_f) for every f > j (in this order).
+ * w_bf16 [n][k]; u [k][k] from gptq_hessian_factor; codes/scales/zeros out
+ * exactly as quantize_groupwise lays them out (w4a16_gemv and w8a16_gemv
+ * consume them). bits 4 or 8; group a multiple of 128 dividing k; k at most
+ * 65536. workspace: at least gptq_workspace_bytes(0, n, k) bytes (an fp32
+ * copy of W and the block's scaled errors), 256-byte aligned, scratch.
+ */
+lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                        int64_t group, void *workspace, int64_t workspace_bytes, void *codes, float *scales,
+                        float *zeros, void *stream);
+
+/*
  * act_absmean -- the per-channel activation magnitude AWQ scales by
  * ("3.6 Quantization", AWQ section: s_X, the average activation magnitude of
  * each input channel over the calibration data; PTQ concept page, AWQ step 1):

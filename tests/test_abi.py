@@ -209,3 +209,31 @@ def test_mxfp4_entry_points_reject(lib):
     assert lib.mxfp4_gemv(A16, 1, B16, MIS, 8, 256, D16, None) == 1
     assert lib.mxfp4_gemv(A16, 1, B16, C16, 8, 256, A16, None) == 1  # y aliases x
     assert lib.mxfp4_gemv(A16, 0, B16, C16, 8, 256, D16, None) == 0
+
+
+def test_gptq_entry_points_reject(lib):
+    ws, ws_bytes, u = P(7 << 20), 1 << 30, P(9 << 20)
+    assert lib.gptq_workspace_bytes(0, 0, 256) == 0
+    assert lib.gptq_workspace_bytes(-1, 4, 256) == -1
+    f = lambda **kw: lib.gptq_hessian_factor(kw.get("x", A16), kw.get("t", 32), kw.get("k", 256),
+                                             ctypes.c_float(kw.get("pd", 0.01)), kw.get("ws", ws),
+                                             kw.get("wsb", ws_bytes), kw.get("u", u), None)
+    assert f(t=0) == 1
+    assert f(pd=0.0) == 1
+    assert f(pd=2.0) == 1
+    assert f(k=200) == 2
+    assert f(x=MIS) == 1
+    assert f(wsb=100) == 1
+    assert f(u=P(1 << 20)) == 1                  # u overlaps x
+    q = lambda **kw: lib.gptq_quantize(kw.get("w", A16), kw.get("n", 8), kw.get("k", 256), kw.get("u", u),
+                                       kw.get("bits", 4), kw.get("sym", 0), kw.get("group", 128), kw.get("ws", ws),
+                                       kw.get("wsb", ws_bytes), kw.get("codes", B16), kw.get("scales", C16),
+                                       kw.get("zeros", D16), None)
+    assert q(bits=3) == 1
+    assert q(group=64) == 2
+    assert q(sym=1) == 1                         # zeros given for symmetric
+    assert q(wsb=10) == 1
+    assert q(codes=P(9 << 20)) == 1              # codes overlap u
+    assert q(n=0, w=None, codes=None) == 0
+    if torch.cuda.device_count() == 0:
+        assert f() == 4 and q() == 4
