@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # fp32 vector, published
 DOMINANT_SRC = os.path.join(ROOT, "bit_gemv_amd", "csrc", "gemv.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "gemv_w4a16_llama70b_counters.json")
 
@@ -253,6 +254,50 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
                           "frac_of_bf16_peak": round(tot_fl / (tot_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                           "linears": awq}
     del xs_k
+    torch.cuda.empty_cache()
+
+    # f2: GPTQ over the Llama-2-7B layer with the AWQ workload's calibration
+    # activations (512 tokens): one factor per input width (4096 and 11008),
+    # then the column loop of each linear, INT4 asymmetric G = 128
+    gq = {}
+    us = {}
+    fl_fac = fl_loop = 0.0
+    t_fac = t_loop = 0.0
+    for kk in sorted({lin.k for lin in aw.linears}):
+        x = dev_bf16(aw.activation(kk, aw.tokens))
+        ws = torch.empty(lib.gptq_workspace_bytes(aw.tokens, 0, kk), dtype=torch.uint8, device=dev)
+        out = {}
+
+        def factor():
+            out["u"] = bg.gptq_hessian_factor(x, workspace=ws)
+
+        ms = _timed(factor, reps=2)
+        us[kk] = out["u"]
+        # H on bf16 MFMA (2 t k^2), reverse Cholesky and inverse (about 2 k^3 / 3 each)
+        fl = 2.0 * aw.tokens * kk * kk + 4.0 * kk ** 3 / 3
+        fl_fac += fl
+        t_fac += ms
+        gq[f"factor k={kk}"] = {"ms": round(ms, 3), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+        log(f"[bench] gptq_hessian_factor k={kk}: {ms:.2f} ms")
+        del x, ws
+    for i, lin in enumerate(aw.linears):
+        w = dev_bf16(aw.weight(0, i))
+        ws = torch.empty(lib.gptq_workspace_bytes(0, lin.n, lin.k), dtype=torch.uint8, device=dev)
+        ms = _timed(lambda: bg.gptq_quantize(w, us[lin.k], 4, aw.symmetric, aw.group, workspace=ws), reps=2)
+        # the lazy updates: about n k^2 flops (fused multiply-adds of the later columns)
+        fl = 1.0 * lin.n * lin.k * lin.k
+        fl_loop += fl
+        t_loop += ms
+        gq[f"{lin.name} {lin.n}x{lin.k}"] = {"ms": round(ms, 3), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+        log(f"[bench] gptq_quantize {lin.name} {lin.n}x{lin.k}: {ms:.2f} ms")
+        del w, ws
+    rows["gptq"] = {"workload": aw.name, "tokens": aw.tokens, "bound": "alu (fp32 FMA) + mfma (H)",
+                    "quant": f"INT4 {'sym' if aw.symmetric else 'asym'} G={aw.group}",
+                    "layer_ms": round(t_fac + t_loop, 3), "factor_ms": round(t_fac, 3), "loop_ms": round(t_loop, 3),
+                    "loop_TFLOPs": round(fl_loop / (t_loop * 1e-3) / 1e12, 2),
+                    "loop_frac_of_fp32_peak": round(fl_loop / (t_loop * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                    "steps": gq}
+    del us
     torch.cuda.empty_cache()
 
     # a5: dequantize (fp32 out) of one matrix per layer, across distinct layers
