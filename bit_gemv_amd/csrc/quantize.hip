@@ -308,42 +308,45 @@ __global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restri
     }
 }
 
-// x_hat = (q - z) * s, 8 consecutive elements per lane.
+// x_hat = (q - z) * s. A wave takes 512 consecutive elements and lane l the
+// elements 4 l .. 4 l + 3 and 256 + 4 l .. + 3 of them, so each of its two
+// 16-byte stores covers 1 KB of contiguous output (the output is 7 of every
+// 8 bytes moved for INT4).
 template <int BITS, bool SYM>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                        const float *__restrict__ scales,
                                                        const float *__restrict__ zeros,
-                                                       int64_t total8, int64_t group,
+                                                       int64_t total, int64_t group,
                                                        float *__restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total8) return;
-    const int64_t elem = i * 8;
-    const int64_t g = elem / group;  // groups tile the flattened matrix
-    const float s = scales[g];
-    const float z = SYM ? 0.0f : zeros[g];
-    int q[8];
-    if (BITS == 4) {
-        const uint32_t word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + elem / 2));
+    const int lane = threadIdx.x & 63;
+    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int u = (int)((word >> (4 * j)) & 0xF);
-            q[j] = SYM ? u - 8 : u;
-        }
-    } else {
-        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(codes + elem));
+    for (int h = 0; h < 2; ++h) {
+        const int64_t elem = base + 256 * h + 4 * lane;  // total is a multiple of 128
+        if (elem >= total) continue;
+        const int64_t g = elem / group;  // groups tile the flattened matrix
+        const float s = scales[g];
+        const float z = SYM ? 0.0f : zeros[g];
+        int q[4];
+        if (BITS == 4) {
+            const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(codes + elem / 2));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t b0 = (v.x >> (8 * j)) & 0xFF, b1 = (v.y >> (8 * j)) & 0xFF;
-            q[j] = SYM ? (int)(int8_t)b0 : (int)b0;
-            q[j + 4] = SYM ? (int)(int8_t)b1 : (int)b1;
+            for (int j = 0; j < 4; ++j) {
+                const int u = (int)((v >> (4 * j)) & 0xF);
+                q[j] = SYM ? u - 8 : u;
+            }
+        } else {
+            const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + elem));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t b = (v >> (8 * j)) & 0xFF;
+                q[j] = SYM ? (int)(int8_t)b : (int)b;
+            }
         }
+        __builtin_nontemporal_store(f32x4{((float)q[0] - z) * s, ((float)q[1] - z) * s, ((float)q[2] - z) * s,
+                                          ((float)q[3] - z) * s},
+                                    reinterpret_cast<f32x4 *>(out + elem));
     }
-    float o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = ((float)q[j] - z) * s;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(out + elem);
-    __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, dst);
-    __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, dst + 1);
 }
 
 template <int BITS, bool SYM, bool CS>
@@ -372,10 +375,10 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t st) {
 
 template <int BITS, bool SYM>
 static hipError_t launch_dequant_t(const DequantArgs &a, hipStream_t st) {
-    const int64_t total8 = a.n * a.k / 8;
-    const int64_t blocks = (total8 + 255) / 256;
+    const int64_t total = a.n * a.k;
+    const int64_t blocks = (total + 2047) / 2048;
     hipLaunchKernelGGL((dequant_kernel<BITS, SYM>), dim3((uint32_t)blocks), dim3(256), 0, st,
-                       a.codes, a.scales, a.zeros, total8, a.group, a.out);
+                       a.codes, a.scales, a.zeros, total, a.group, a.out);
     return hipGetLastError();
 }
 

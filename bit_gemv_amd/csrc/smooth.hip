@@ -16,65 +16,81 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
-// Column maxima of |W| over rows, folded into s[] with atomicMax on the
-// bit patterns (non-negative floats order like their bits, and max is exact
-// and order-free, so the result is deterministic).
-// Block: 256 lanes x 8 columns = 2048 columns, `rows` rows.
-__global__ __launch_bounds__(256) void colmax_kernel(const uint16_t *__restrict__ w, int64_t n, int64_t k,
-                                                      int rows, uint32_t *__restrict__ acc) {
-    const int64_t col = (int64_t)blockIdx.x * 2048 + threadIdx.x * 8;
-    if (col >= k) return;
-    const int64_t r0 = (int64_t)blockIdx.y * rows;
-    const int64_t r1 = r0 + rows < n ? r0 + rows : n;
-    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int64_t r = r0;
-    for (; r + 4 <= r1; r += 4) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w + (r + u) * k + col));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            m[0] = fmaxf(m[0], fabsf(bf16_lo(v[u].x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v[u].x)));
-            m[2] = fmaxf(m[2], fabsf(bf16_lo(v[u].y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v[u].y)));
-            m[4] = fmaxf(m[4], fabsf(bf16_lo(v[u].z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v[u].z)));
-            m[6] = fmaxf(m[6], fabsf(bf16_lo(v[u].w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v[u].w)));
-        }
-    }
-    for (; r < r1; ++r) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(w + r * k + col);
-        m[0] = fmaxf(m[0], fabsf(bf16_lo(v.x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v.x)));
-        m[2] = fmaxf(m[2], fabsf(bf16_lo(v.y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v.y)));
-        m[4] = fmaxf(m[4], fabsf(bf16_lo(v.z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v.z)));
-        m[6] = fmaxf(m[6], fabsf(bf16_lo(v.w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v.w)));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) atomicMax(acc + col + i, __float_as_uint(m[i]));
+// |v| of 8 bf16 values (one 16-byte word) folded into running maxima.
+LQ_DEVICE void max8(float *m, const u32x4 v) {
+    m[0] = fmaxf(m[0], fabsf(bf16_lo(v.x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v.x)));
+    m[2] = fmaxf(m[2], fabsf(bf16_lo(v.y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v.y)));
+    m[4] = fmaxf(m[4], fabsf(bf16_lo(v.z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v.z)));
+    m[6] = fmaxf(m[6], fabsf(bf16_lo(v.w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v.w)));
 }
 
-// Column maxima of |X| (128 columns per block: 16 lanes x 8 columns, 16 row
-// phases reduced through LDS), then s = f(ax, aw) with aw read from s[].
+// Column maxima of |W| over rows, folded into s[] with atomicMax on the
+// bit patterns (non-negative floats order like their bits, and max is exact
+// and order-free, so the result is deterministic). Block: 512 columns (a
+// wave's 64 lanes x 8) x kColRows rows, the 4 waves taking every 4th row
+// with 8 rows' loads in flight per lane; the waves' maxima meet in LDS, so
+// each block issues one atomic per column.
+constexpr int kColRows = 128;
+
+__global__ __launch_bounds__(256) void colmax_kernel(const uint16_t *__restrict__ w, int64_t n, int64_t k,
+                                                      uint32_t *__restrict__ acc) {
+    __shared__ float red[4][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
+    const int64_t r1 = r0 + kColRows < n ? r0 + kColRows : n;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (col < k) {
+        for (int64_t r = r0 + wave; r < r1; r += 32) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t rr = r + 4 * u;
+                v[u] = rr < r1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w + rr * k + col))
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) max8(m, v[u]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = threadIdx.x + 256 * h;
+        const float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        if ((int64_t)blockIdx.x * 512 + c < k) atomicMax(acc + (int64_t)blockIdx.x * 512 + c, __float_as_uint(v));
+    }
+}
+
+// Column maxima of |X| (32 columns per block: 4 lanes x 8 columns, 64 row
+// phases with 8 rows' loads in flight, reduced through LDS), then
+// s = f(ax, aw) with aw read from s[].
 __global__ __launch_bounds__(256) void smooth_finalize_kernel(const uint16_t *__restrict__ x, int64_t t,
                                                                int64_t k, float alpha,
                                                                float *__restrict__ s) {
-    __shared__ float red[16][129];
-    const int cl = threadIdx.x & 15, ph = threadIdx.x >> 4;
-    const int64_t col = (int64_t)blockIdx.x * 128 + cl * 8;
+    __shared__ float red[64][33];
+    const int cl = threadIdx.x & 3, ph = threadIdx.x >> 2;
+    const int64_t col = (int64_t)blockIdx.x * 32 + cl * 8;
     float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int64_t r = ph; r < t; r += 16) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(x + r * k + col);
-        m[0] = fmaxf(m[0], fabsf(bf16_lo(v.x))); m[1] = fmaxf(m[1], fabsf(bf16_hi(v.x)));
-        m[2] = fmaxf(m[2], fabsf(bf16_lo(v.y))); m[3] = fmaxf(m[3], fabsf(bf16_hi(v.y)));
-        m[4] = fmaxf(m[4], fabsf(bf16_lo(v.z))); m[5] = fmaxf(m[5], fabsf(bf16_hi(v.z)));
-        m[6] = fmaxf(m[6], fabsf(bf16_lo(v.w))); m[7] = fmaxf(m[7], fabsf(bf16_hi(v.w)));
+    for (int64_t r = ph; r < t; r += 512) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t rr = r + 64 * u;
+            v[u] = rr < t ? *reinterpret_cast<const u32x4 *>(x + rr * k + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) max8(m, v[u]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[ph][cl * 8 + i] = m[i];
     __syncthreads();
-    if (threadIdx.x < 128) {
+    if (threadIdx.x < 32) {
         float ax = red[0][threadIdx.x];
-        for (int p = 1; p < 16; ++p) ax = fmaxf(ax, red[p][threadIdx.x]);
-        const int64_t j = (int64_t)blockIdx.x * 128 + threadIdx.x;
+        for (int p = 1; p < 64; ++p) ax = fmaxf(ax, red[p][threadIdx.x]);
+        const int64_t j = (int64_t)blockIdx.x * 32 + threadIdx.x;
         float aw = s[j];  // the column max of |W| left by colmax_kernel
         const float a = ax < kFloor ? kFloor : ax;
         const float b = aw < kFloor ? kFloor : aw;
@@ -92,11 +108,10 @@ hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3((uint32_t)((a.k + 255) / 256)), dim3(256), 0, st, acc, a.k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int rows = 64;
-    dim3 grid((uint32_t)((a.k + 2047) / 2048), (uint32_t)((a.n + rows - 1) / rows));
-    hipLaunchKernelGGL(colmax_kernel, grid, dim3(256), 0, st, a.w, a.n, a.k, rows, acc);
+    dim3 grid((uint32_t)((a.k + 511) / 512), (uint32_t)((a.n + kColRows - 1) / kColRows));
+    hipLaunchKernelGGL(colmax_kernel, grid, dim3(256), 0, st, a.w, a.n, a.k, acc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(smooth_finalize_kernel, dim3((uint32_t)(a.k / 128)), dim3(256), 0, st, a.x, a.t, a.k,
+    hipLaunchKernelGGL(smooth_finalize_kernel, dim3((uint32_t)(a.k / 32)), dim3(256), 0, st, a.x, a.t, a.k,
                        a.alpha, a.s);
     return hipGetLastError();
 }
