@@ -135,7 +135,12 @@ lq_status dequantize_groupwise(const void *codes, const float *scales, const flo
  *         use w4a16_gemm).
  * codes   [n][k/2] INT4 codes from quantize_groupwise(bits = 4).
  * scales  fp32 [n][k/group]; zeros fp32 [n][k/group] or NULL if symmetric.
- * y       out fp32 [b][n].
+ * y       out fp32 [b][n], device memory (coarse-grained: for batch 4..16 on
+ *         matrices of about 40M weights and more with few row blocks, the
+ *         kernel splits k, zeroes y on `stream` and adds partial sums into
+ *         it with float atomics; with more than two such runs the
+ *         summation order, and so the last bits of y, can vary from call
+ *         to call. Every other case is deterministic).
  * group: multiple of 128 dividing k; k multiple of 128 and at most 2^28.
  */
 lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales,

@@ -51,14 +51,50 @@ def test_batches(b, sym):
 
 @pytest.mark.parametrize("b", [5, 16])
 @pytest.mark.parametrize("sym", [False, True])
-@pytest.mark.parametrize("n,k", [(4096 + 17, 11008), (12288, 4096), (33, 128), (1000, 128 * 37), (64, 28672),
-                                 (12288 + 5, 2048 + 128), (16384 + 33, 4096 + 384)])
+@pytest.mark.parametrize("n,k", [(4096 + 17, 4096), (8192, 4096), (33, 128), (1000, 128 * 37), (64, 28672),
+                                 (12288 + 5, 2048 + 128), (16384 + 33, 2048 + 128), (20000, 2048)])
 def test_mfma_batches(n, k, b, sym):
-    """Batches 5..16 on the matrix-core kernels: the LDS-ring kernel (n up to
+    """Batches 5..16 below about 40M weights: the LDS-ring kernel (n up to
     12288: ragged 16-row tiles, a half last 256-wide stage, waves with no
     stage) and the register-streaming kernel for taller matrices (ragged
     tiles, uneven group runs)."""
     _case(n, k, b, sym, seed=n % 89 + b)
+
+
+# (n, k): blocks of 128 rows x runs of 256-wide stages in the shared-stage
+# kernel (about 40M weights and more; batch 4 only when n or k >= 16384)
+SHARED_SHAPES = [
+    (16384 + 33, 4096 + 384),   # ragged rows, half last stage, 2 runs
+    (4096 + 17, 11008),         # 8 runs of 6 stages, the last with 1
+    (1000, 45056),              # 32 runs of 6 stages: the last two empty
+    (8192 + 100, 8192 - 128),   # 4 runs, half last stage
+    (12288, 4096),              # 2 runs, whole blocks and stages
+    (40000 + 77, 2048 + 128),   # no split, half last stage
+]
+
+
+@pytest.mark.parametrize("b", [4, 5, 8, 9, 16])
+@pytest.mark.parametrize("n,k", SHARED_SHAPES)
+def test_shared_stage_batches(n, k, b):
+    """Batch rows staged 4, 8 or 16 at a time (rows past the batch read
+    zeros), asymmetric; split runs add into y through atomics."""
+    if b == 4 and max(n, k) < 16384:
+        pytest.skip("batch 4 takes the VALU kernel on this shape")
+    _case(n, k, b, False, seed=n % 83 + b)
+
+
+@pytest.mark.parametrize("b", [4, 12])
+@pytest.mark.parametrize("n,k", [(16384 + 33, 4096 + 384), (1000, 45056), (40000 + 77, 2048 + 128)])
+def test_shared_stage_symmetric(n, k, b):
+    _case(n, k, b, True, seed=n % 79 + b)
+
+
+@pytest.mark.parametrize("group", [256, 1024, "k"])
+def test_shared_stage_larger_groups(group):
+    """A group spans both halves of a stage (or several stages); each half
+    reads its own group's scale."""
+    n, k = 10240 + 3, 8192
+    _case(n, k, 16, False, group=k if group == "k" else group, seed=7)
 
 
 @pytest.mark.parametrize("b", [6, 16])
@@ -106,3 +142,27 @@ def test_batch_over_16_is_unsupported():
     with pytest.raises(bg.LibquantError) as e:
         bg.w4a16_gemv(x, pw)
     assert e.value.status == bg.LQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n,k,runs", [(16384 + 33, 4096 + 384, 2), (1000, 45056, 32)])
+def test_shared_stage_overwrites_y(n, k, runs):
+    """Split runs add into y after it is zeroed on the same stream: a y full
+    of NaN is overwritten, and a second call into the same y gives the same
+    result (bit for bit with two runs, where 0 + a + b does not depend on
+    the order; to rounding with more)."""
+    import torch
+    rng = np.random.default_rng(n + k)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    x = f32_to_bf16_bits(rng.standard_normal((16, k)))
+    say(f"gemv shared-stage y overwrite n={n} k={k} runs={runs}")
+    pw = bg.quantize_groupwise(dev_bf16(w), 4, False, 128)
+    c_ref, s_ref, z_ref = oracle.quantize(w, 4, False, 128)
+    y_ref = oracle.w4a16_matmul(x, c_ref, s_ref, z_ref, n, k, False, 128)
+    y = torch.full((16, n), float("nan"), dtype=torch.float32, device="cuda")
+    xd = dev_bf16(x)
+    first = host(bg.w4a16_gemv(xd, pw, y)).copy()
+    assert_close(first, y_ref, "first call")
+    second = host(bg.w4a16_gemv(xd, pw, y))
+    assert_close(second, y_ref, "second call")
+    if runs == 2:
+        assert np.array_equal(first.view(np.uint32), second.view(np.uint32))
