@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libquant.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "gemv8.hip", "gemm.hip", "smooth.hip", "w8a8.hip", "awq.hip", "mx.hip", "gptq.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "gemv_shared.hip", "gemv8.hip", "gemm.hip", "smooth.hip", "w8a8.hip", "awq.hip", "mx.hip", "gptq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -41,6 +41,7 @@ EXTRA = {
     "w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemv_shared.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "awq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

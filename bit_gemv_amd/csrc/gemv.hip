@@ -1,6 +1,5 @@
 // gemv.hip -- W4A16 decode GEMV for gfx950: a VALU (v_dot2_f32_bf16) kernel
-// for batch 1..4 and MFMA (16x16x32 bf16) kernels for batch 5..16 (and
-// batch 4 on the largest matrices).
+// for batch 1..4 and MFMA (16x16x32 bf16) kernels for batch 5..16.
 //
 // Definition ("LLM quantization deep dive", rainlib.com, W4A16: INT4 weights
 // in memory, unpacked and dequantized inside the kernel and multiplied with
@@ -21,9 +20,8 @@
 //  * Nibbles 0..3 of a code word pair with nibbles 4..7, so activations are
 //    re-paired (x0, x4), (x1, x5), ... when loaded.
 // Partial sums are reduced with butterflies inside a wave and through LDS
-// across waves. Only the shared-stage kernel, when it splits k into more
-// than two runs, adds into y with atomics (its own comment says when); every
-// other path is deterministic.
+// across waves; no atomics, so results are deterministic. Batch 4..16 on
+// large matrices goes to the shared-stage kernel of gemv_shared.hip instead.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -567,202 +565,6 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     }
 }
 
-// ---------------------------------------------------------------------------
-// Shared-stage kernel, batch 4..16 on large matrices
-// (v_mfma_f32_16x16x32_bf16, operands through LDS).
-// The ring kernel gives each wave its own 16-row tile, so every wave loads
-// the whole activation stage for 16 rows of codes, and the register kernel
-// re-reads activation fragments from L2 for every 32 rows: at batch 16 the
-// activation traffic reaches a third of the code traffic. Here a block of 4
-// waves works on kShRows = 128 rows together and shares each 256-wide stage
-// in LDS: per stage every wave issues 4 of the block's 16 code loads (8 rows
-// x 128 bytes each), a share of the XR activation rows, and a quarter of
-// the 2 groups x 128 rows of scales (and zeros), all as buffer loads in the
-// LDS-write form. Three slots: one stage is computed while the next is in
-// flight; the stage wait is the block's own vmcnt followed by a barrier
-// (loads that write LDS are only counted by vmcnt), and the slot refilled
-// after it is the one every wave finished in the previous iteration.
-// Wave w computes rows 32 w .. 32 w + 31 of the block as two 16-row MFMA
-// tiles sharing the activation operand; per 128-wide group the tile D_g and
-// the activation sums X_g (an MFMA against a bf16 ones operand) give
-// acc += s (D_g - (128 + z) X_g), as in the other matrix-core kernels.
-// LDS layout of a slot: codes [128 rows][128 B], 16-byte chunk c of row r
-// stored at c ^ ((r >> 1) & 7); activations [XR rows][512 B], chunk c of row
-// r at c ^ r (batch column b reads row b % XR; rows past the batch read
-// zeros and columns past it are never stored); scales, then zeros,
-// [2][128] fp32 (group of the stage, row). With these the 16 rows (columns)
-// of one fragment read fall in distinct banks. 2 blocks fit on a CU.
-// With too few row blocks to fill the chip, k is split into runs of stages
-// (blockIdx.y); the runs add their partial sums into y, zeroed first, with
-// float atomics, so with more than two runs the summation order (and the
-// last bits of y) can differ from call to call.
-// ---------------------------------------------------------------------------
-constexpr int kShRows = 128;   // rows per block (32 per wave)
-constexpr int kShStageK = 256;
-constexpr int kShSlots = 3;
-
-template <int XR, bool SYM, bool SPLIT>
-__global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__restrict__ x, int bsz,
-                                                           const uint8_t *__restrict__ codes,
-                                                           const float *__restrict__ scales,
-                                                           const float *__restrict__ zeros, int n, int k,
-                                                           int group, int stages_per_run, float *__restrict__ y) {
-    constexpr int kXPieces = XR / 2;                                  // 1 KB activation pieces per stage
-    constexpr int kXPerWave = kXPieces >= 4 ? kXPieces / 4 : 1;       // issued by each wave
-    constexpr int kCodes = kShRows * 128;
-    constexpr int kXOff = kCodes, kSOff = kXOff + XR * 512, kDummy = kSOff + kShRows * 16;
-    constexpr int kSlot = kDummy + (kXPieces < 4 * kXPerWave ? 1024 : 0);  // a sink for waves without a piece
-    constexpr int kLoads = 4 + kXPerWave + (SYM ? 1 : 2);             // per wave per stage
-    constexpr int kVm = (kShSlots - 2) * kLoads;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kShSlots * kSlot];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l16 = lane & 15, kq = lane >> 4;
-    const int row0 = blockIdx.x * kShRows;
-    const int ng = k / group;
-    const uint32_t row_bytes = (uint32_t)k / 2;
-    const int nst = (k + kShStageK - 1) / kShStageK;
-    const int s0 = blockIdx.y * stages_per_run;
-    const int s1 = min(nst, s0 + stages_per_run);
-    const int rows_here = min(kShRows, n - row0);
-    // rows past n, k past the row and batch rows past bsz read zeros
-    const auto rc = make_rsrc(codes + (int64_t)row0 * row_bytes, (uint32_t)rows_here * row_bytes);
-    const auto rx = make_rsrc(x, (uint32_t)bsz * (uint32_t)k * 2);
-    const auto rs = make_rsrc(scales + (int64_t)row0 * ng, (uint32_t)(rows_here * ng) * 4);
-    const auto rz = make_rsrc(SYM ? scales : zeros + (int64_t)row0 * ng, SYM ? 0u : (uint32_t)(rows_here * ng) * 4);
-
-    // code piece p = 4 wave + i: rows 8 p + lane / 8, stored chunk lane % 8
-    uint32_t c_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (4 * wave + i) + (lane >> 3);
-        c_off[i] = (uint32_t)r * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
-    }
-    // activation piece q: rows 2 q + lane / 32, stored chunk lane % 32
-    // (fixed-size arrays: a lambda capturing an array whose size depends on
-    // a template parameter is dropped from the host compilation)
-    static_assert(kXPerWave <= 2, "activation pieces per wave");
-    uint32_t x_off[2];
-    bool x_real[2];
-#pragma unroll
-    for (int i = 0; i < kXPerWave; ++i) {
-        const int q = kXPerWave * wave + i;
-        const int xr = 2 * q + (lane >> 5);
-        x_real[i] = q < kXPieces;
-        x_off[i] = (uint32_t)xr * (uint32_t)k * 2 + 16u * (uint32_t)((lane & 31) ^ xr);
-    }
-    // scale entry e = 64 wave + lane: group e / 128 of the stage, row e % 128
-    const int se = 64 * wave + lane;
-    const int s_half = se / kShRows, s_row = se % kShRows;
-
-    auto issue = [&](int st) {
-        uint8_t *slot = ring + (st % kShSlots) * kSlot;
-        const bool in = st < s1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rc, (__attribute__((address_space(3))) void *)(slot + 1024 * (4 * wave + i)), 16,
-                in ? c_off[i] + (uint32_t)st * 128 : kOutOfRange, 0, 0, kNonTemporal);
-#pragma unroll
-        for (int i = 0; i < kXPerWave; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx,
-                (__attribute__((address_space(3))) void *)(slot + (x_real[i] ? kXOff + 1024 * (kXPerWave * wave + i)
-                                                                             : kDummy)),
-                16, in && x_real[i] ? x_off[i] + (uint32_t)st * 512 : kOutOfRange, 0, 0, 0);
-        const int kk = st * kShStageK + 128 * s_half;
-        const uint32_t so =
-            in && kk < k && s_row < rows_here ? (uint32_t)(s_row * ng + kk / group) * 4 : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(slot + kSOff + 256 * wave),
-                                                 4, so, 0, 0, 0);
-        if (!SYM)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rz, (__attribute__((address_space(3))) void *)(slot + kSOff + kShRows * 8 + 256 * wave), 4, so, 0, 0,
-                0);
-    };
-
-    uint32_t magic;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4{kOnes, kOnes, kOnes, kOnes});
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    // fragment reads: A = codes of row 32 wave + 16 t + lane % 16, group h,
-    // k quarter lane / 16; B = activation row (lane % 16) % XR, same k
-    int a_off[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = 32 * wave + 16 * t + l16;
-            a_off[t][h] = r * 128 + 16 * ((4 * h + kq) ^ ((r >> 1) & 7));
-        }
-    const int xrow = l16 % XR;
-    int b_off[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b_off[h][j] = kXOff + xrow * 512 + 16 * ((16 * h + 4 * kq + j) ^ xrow);
-
-#pragma unroll
-    for (int i = 0; i < kShSlots - 1; ++i) issue(s0 + i);
-    for (int st = s0; st < s1; ++st) {
-        // stage st has landed for every wave; the slot refilled below was
-        // last read in the previous iteration, before this barrier
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
-        issue(st + kShSlots - 1);
-        const uint8_t *slot = ring + (st % kShSlots) * kSlot;
-        const float *sz = reinterpret_cast<const float *>(slot + kSOff);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8_t bop[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bop[j] = *reinterpret_cast<const bf16x8_t *>(slot + b_off[h][j]);
-            f32x4 xg = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bop[j], xg, 0, 0, 0);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x4 cw = *reinterpret_cast<const u32x4 *>(slot + a_off[t][h]);
-                const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-                f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, unpack_natural(w[j], magic)),
-                                                                bop[j], d, 0, 0, 0);
-                const int rb = h * kShRows + 32 * wave + 16 * t + 4 * kq;
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(&sz[rb]);
-                f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (!SYM) zv = *reinterpret_cast<const f32x4 *>(&sz[2 * kShRows + rb]);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float c = SYM ? 136.0f : 128.0f + zv[v];
-                    acc[t][v] = __builtin_fmaf(sv[v], __builtin_fmaf(-c, xg[v], d[v]), acc[t][v]);
-                }
-            }
-        }
-    }
-    // the loads issued past the last stage (zeros into spare slots) land
-    // before the block ends
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = row0 + 32 * wave + 16 * t + 4 * kq + v;
-            if (row < n && l16 < bsz) {
-                float *dst = y + (int64_t)l16 * n + row;
-                if (SPLIT)
-                    atomicAdd(dst, acc[t][v]);
-                else
-                    *dst = acc[t][v];
-            }
-        }
-}
-
-__global__ void gemv_zero_kernel(float *__restrict__ p, int64_t count) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < count) p[i] = 0.0f;
-}
-
 template <int B, int RW, bool SYM>
 static hipError_t launch_valu_rw(const WoArgs &a, hipStream_t st, int ks_count) {
     // staged scales need whole 4-group runs per row: k a multiple of 512
@@ -806,55 +608,10 @@ static hipError_t launch_mfma(const WoArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// The shared-stage kernel pays off on large matrices (measured on MI355X,
-// 1.1-2.1x over the kernels below): batch 5..16 from about 40M weights,
-// batch 4 from there when the matrix is also tall or long (n or k >= 16384).
-// It addresses a block's codes (128 rows) and the activations with 32-bit
-// offsets below 2^31.
-static bool shared_pays(const WoArgs &a) {
-    if (a.m < 4 || a.k * 64 >= (int64_t(1) << 31) || a.m * a.k * 2 >= (int64_t(1) << 31)) return false;
-    const bool large = a.n * a.k >= (int64_t(40) << 20);
-    return a.m >= 5 ? large : large && (a.n >= 16384 || a.k >= 16384);
-}
-
-// Runs of k: the smallest power of two that gives 160 blocks or more, with
-// at least 4 stages per run. XR: the batch rounded up to 4, 8 or 16.
-template <bool SYM>
+// Batch 4..16 on large matrices: the shared-stage kernel of gemv_shared.hip.
 static hipError_t launch_shared(const WoArgs &a, hipStream_t st) {
-    const int64_t blocks = (a.n + kShRows - 1) / kShRows;
-    const int nst = (int)((a.k + kShStageK - 1) / kShStageK);
-    int runs = 1;
-    while (blocks * runs < 160 && runs * 2 <= nst / 4) runs *= 2;
-    const int per = (nst + runs - 1) / runs;
-    const dim3 grid((uint32_t)blocks, (uint32_t)runs);
-    if (runs > 1) {
-        const int64_t count = a.m * a.n;
-        hipLaunchKernelGGL(gemv_zero_kernel, dim3((uint32_t)((count + 255) / 256)), dim3(256), 0, st, a.y, count);
-    }
-#define LQ_SHARED(XR, SPLIT)                                                                                      \
-    hipLaunchKernelGGL((gemv_shared_kernel<XR, SYM, SPLIT>), grid, dim3(256), 0, st, a.x, (int)a.m, a.codes,    \
-                       a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, per, a.y)
-    if (a.m <= 4) {
-        if (runs > 1) {
-            LQ_SHARED(4, true);
-        } else {
-            LQ_SHARED(4, false);
-        }
-    } else if (a.m <= 8) {
-        if (runs > 1) {
-            LQ_SHARED(8, true);
-        } else {
-            LQ_SHARED(8, false);
-        }
-    } else {
-        if (runs > 1) {
-            LQ_SHARED(16, true);
-        } else {
-            LQ_SHARED(16, false);
-        }
-    }
-#undef LQ_SHARED
-    return hipGetLastError();
+    const SharedGemvArgs sa{a.x, a.m, a.codes, a.scales, a.zeros, a.n, a.k, a.symmetric, a.group, a.y};
+    return launch_shared_gemv(WeightFormat::kInt4, sa, st);
 }
 
 // Batch 5..16 elsewhere (measured on MI355X): the LDS-ring kernel while
@@ -863,7 +620,7 @@ static hipError_t launch_shared(const WoArgs &a, hipStream_t st) {
 // register-streaming MFMA kernel for taller matrices.
 template <bool SYM>
 static hipError_t launch_batch(const WoArgs &a, hipStream_t st) {
-    if (shared_pays(a)) return launch_shared<SYM>(a, st);
+    if (shared_gemv_pays(WeightFormat::kInt4, a.m, a.n, a.k)) return launch_shared(a, st);
     if (a.n <= 12288 && a.m * a.k * 2 < (int64_t(1) << 32)) {
         if (a.m <= 8)
             hipLaunchKernelGGL((gemv_ring_kernel<8, SYM>), dim3((uint32_t)((a.n + 15) / 16)), dim3(256), 0, st, a.x,
@@ -882,7 +639,9 @@ static hipError_t launch_gemv_s(const WoArgs &a, hipStream_t st) {
         case 1: return launch_valu<1, SYM>(a, st);
         case 2: return launch_valu<2, SYM>(a, st);
         case 3: return launch_valu<3, SYM>(a, st);
-        case 4: return shared_pays(a) ? launch_shared<SYM>(a, st) : launch_valu<4, SYM>(a, st);
+        case 4:
+            return shared_gemv_pays(WeightFormat::kInt4, a.m, a.n, a.k) ? launch_shared(a, st)
+                                                                        : launch_valu<4, SYM>(a, st);
         default: return launch_batch<SYM>(a, st);
     }
 }

@@ -28,7 +28,8 @@
 // rows and one 4-byte scale (and zero) load per lane covering RW rows x 8
 // groups, then computes. Per-row partial sums stay in registers until one
 // reduction inside the wave and one through LDS; no atomics, so results are
-// deterministic.
+// deterministic. Batch 5..16 on large matrices goes to the shared-stage
+// kernel of gemv_shared.hip instead.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -227,6 +228,11 @@ static hipError_t launch8_s(const WoArgs &a, hipStream_t st) {
 
 hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st) {
     if (a.m < 1 || a.m > 16) return hipErrorInvalidValue;
+    // batch 5..16 on large matrices: the shared-stage kernel of gemv_shared.hip
+    if (shared_gemv_pays(WeightFormat::kInt8, a.m, a.n, a.k)) {
+        const SharedGemvArgs sa{a.x, a.m, a.codes, a.scales, a.zeros, a.n, a.k, a.symmetric, a.group, a.y};
+        return launch_shared_gemv(WeightFormat::kInt8, sa, st);
+    }
     return a.symmetric ? launch8_s<true>(a, st) : launch8_s<false>(a, st);
 }
 

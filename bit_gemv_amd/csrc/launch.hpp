@@ -105,6 +105,23 @@ struct AwqArgs {
     float *scales, *zeros;
 };
 
+// Decode GEMV at batch 4..16 on large matrices (gemv_shared.hip), for the
+// three weight formats. scales: fp32 [n][k / group] for INT4 and INT8,
+// E8M0 bytes [n][k / 32] for MXFP4 (group and zeros unused there).
+enum class WeightFormat { kInt4, kInt8, kMx };
+
+struct SharedGemvArgs {
+    const uint16_t *x;
+    int64_t m;
+    const uint8_t *codes;
+    const void *scales;
+    const float *zeros;
+    int64_t n, k;
+    int symmetric;
+    int64_t group;
+    float *y;
+};
+
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
 hipError_t launch_w4a16_gemv(const WoArgs &a, hipStream_t st);
@@ -127,5 +144,9 @@ hipError_t launch_gptq_quantize(const GptqArgs &a, hipStream_t st);
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int64_t n, int64_t k, float *y,
                             hipStream_t st);
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
+// Whether the shared-stage kernel is the faster one for this shape, and its
+// launcher (which takes any shape it is given, batch 1..16).
+bool shared_gemv_pays(WeightFormat f, int64_t m, int64_t n, int64_t k);
+hipError_t launch_shared_gemv(WeightFormat f, const SharedGemvArgs &a, hipStream_t st);
 
 }  // namespace lq

@@ -244,6 +244,11 @@ hipError_t launch_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *
 }
 
 hipError_t launch_mx_gemv(const MxArgs &a, hipStream_t st) {
+    // batch 4..16 on large matrices: the shared-stage kernel of gemv_shared.hip
+    if (shared_gemv_pays(WeightFormat::kMx, a.m, a.n, a.k)) {
+        const SharedGemvArgs sa{a.x, a.m, a.codes, a.scales, nullptr, a.n, a.k, 0, 32, a.y};
+        return launch_shared_gemv(WeightFormat::kMx, sa, st);
+    }
     switch (a.m) {
         case 1: return launch_mx<1>(a, st);
         case 2: return launch_mx<2>(a, st);

@@ -62,14 +62,14 @@ def test_mfma_batches(n, k, b, sym):
 
 
 # (n, k): blocks of 128 rows x runs of 256-wide stages in the shared-stage
-# kernel (about 40M weights and more; batch 4 only when n or k >= 16384)
+# kernel (batch 4..16 from about 40M weights)
 SHARED_SHAPES = [
-    (16384 + 33, 4096 + 384),   # ragged rows, half last stage, 2 runs
-    (4096 + 17, 11008),         # 8 runs of 6 stages, the last with 1
-    (1000, 45056),              # 32 runs of 6 stages: the last two empty
-    (8192 + 100, 8192 - 128),   # 4 runs, half last stage
+    (16384 + 33, 4096 + 384),   # ragged rows, half last stage, 4 runs of 5 stages, the last with 3
+    (4096 + 17, 11008),         # 4 runs of 11 stages, the last with 10
+    (1000, 45056),              # 32 runs of 6 stages: one with 2, the last two empty
+    (8192 + 100, 8192 - 128),   # 8 runs of 4 stages, half last stage
     (12288, 4096),              # 2 runs, whole blocks and stages
-    (40000 + 77, 2048 + 128),   # no split, half last stage
+    (40000 + 77, 2048 + 128),   # 314 blocks: no split, half last stage
 ]
 
 
@@ -78,8 +78,6 @@ SHARED_SHAPES = [
 def test_shared_stage_batches(n, k, b):
     """Batch rows staged 4, 8 or 16 at a time (rows past the batch read
     zeros), asymmetric; split runs add into y through atomics."""
-    if b == 4 and max(n, k) < 16384:
-        pytest.skip("batch 4 takes the VALU kernel on this shape")
     _case(n, k, b, False, seed=n % 83 + b)
 
 
@@ -144,7 +142,7 @@ def test_batch_over_16_is_unsupported():
     assert e.value.status == bg.LQ_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("n,k,runs", [(16384 + 33, 4096 + 384, 2), (1000, 45056, 32)])
+@pytest.mark.parametrize("n,k,runs", [(12288, 4096, 2), (1000, 45056, 32)])
 def test_shared_stage_overwrites_y(n, k, runs):
     """Split runs add into y after it is zeroed on the same stream: a y full
     of NaN is overwritten, and a second call into the same y gives the same

@@ -89,6 +89,49 @@ def test_extreme_codes():
         assert_close(y, oracle.w8a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, 128), f"extreme sym={sym}")
 
 
+# Batch 5..8 from about 40M weights and 9..16 from 16M go to the
+# shared-stage kernel: 128-row blocks (ragged here), k in 128-wide stages
+# split into runs (uneven, some empty) whose partial sums meet in y.
+@pytest.mark.parametrize("b", [5, 8, 9, 16])
+@pytest.mark.parametrize("n,k", [(16384 + 33, 4096 + 384),   # 8 runs of 5 stages, the last empty
+                                 (4096 + 17, 11008),         # 16 runs of 6, one with 2, one empty
+                                 (8192 + 100, 8192 - 128),   # 8 runs of 8, the last with 7
+                                 (40000 + 77, 2048 + 128)])  # no split
+def test_shared_stage_batches(n, k, b):
+    _case(n, k, b, False, seed=n % 83 + b)
+
+
+@pytest.mark.parametrize("b", [6, 12])
+@pytest.mark.parametrize("n,k", [(16384 + 33, 4096 + 384), (4096, 4096)])
+def test_shared_stage_symmetric(n, k, b):
+    """Symmetric int8 codes (the 0x80 flip and the constant 128); 4096 x 4096
+    takes the shared-stage kernel only at batch 9 and more."""
+    _case(n, k, b, True, seed=n % 79 + b)
+
+
+@pytest.mark.parametrize("group", [256, 1024, "k"])
+def test_shared_stage_larger_groups(group):
+    n, k = 10240 + 3, 8192
+    _case(n, k, 16, False, group=k if group == "k" else group, seed=7)
+
+
+def test_shared_stage_extreme_codes():
+    """End codes (-127 / 127, 0 / 255) through the shared-stage conversion."""
+    rng = np.random.default_rng(8)
+    n, k = 10240 + 3, 4096
+    w = rng.standard_normal((n, k)) * 0.02
+    w[:, ::128] = 0.5
+    w[:, 1::128] = -0.5
+    wb = f32_to_bf16_bits(w)
+    x = f32_to_bf16_bits(rng.standard_normal((16, k)))
+    for sym in (False, True):
+        say(f"w8a16 shared-stage extreme codes sym={sym}")
+        pw = bg.quantize_groupwise(dev_bf16(wb), 8, sym, 128)
+        c_ref, s_ref, z_ref = oracle.quantize(wb, 8, sym, 128)
+        y = host(bg.w8a16_gemv(dev_bf16(x), pw))
+        assert_close(y, oracle.w8a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, 128), f"extreme sym={sym}")
+
+
 def test_int4_codes_are_refused():
     import torch
     w = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")

@@ -109,3 +109,43 @@ def test_workload_gate_up_sampled_rows():
     assert_same_bits(host(mw.codes)[rows], c_ref, "sampled codes")
     assert_same_bits(host(mw.scales)[rows], s_ref, "sampled scales")
     assert_close(y[:, rows], oracle.mx_matmul(x, c_ref, s_ref, rows.size, k), "sampled y")
+
+
+# Batch 4..8 from about 40M weights and 9..16 from 16M go to the
+# shared-stage kernel, which folds each block's scale into the E2M1 -> bf16
+# conversion: ragged 128-row blocks, half last 256-wide stages, runs of k
+# (some empty), 4, 8 or 16 staged batch rows.
+@pytest.mark.parametrize("b", [4, 5, 8, 9, 16])
+@pytest.mark.parametrize("n,k", [(16384 + 33, 4096 + 384), (4096 + 17, 11008), (1000, 45056),
+                                 (40000 + 77, 2048 + 128)])
+def test_shared_stage_batches(n, k, b):
+    _gemv_case(n, k, b, seed=n % 71 + b, what="shared")
+
+
+@pytest.mark.parametrize("b", [9, 16])
+def test_shared_stage_from_16m_weights(b):
+    _gemv_case(4096, 4096, b, seed=b, what="shared 4096")
+
+
+@pytest.mark.parametrize("b", [5, 16])
+def test_shared_stage_row_magnitudes(b):
+    """Rows scaled by 2^-130 .. 2^90: block scales over most of the E8M0
+    range, and at the low end elements that are bf16 subnormals once scaled
+    (the conversion with the block scale and the MFMA keep them). Each
+    output is checked against its own magnitude, sum_j |x_j w_hat_j|."""
+    n, k = 10240 + 3, 4096
+    rng = np.random.default_rng(20 + b)
+    e = rng.integers(-130, 91, n)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * np.ldexp(1.0, e)[:, None])
+    x = f32_to_bf16_bits(rng.standard_normal((b, k)))
+    mw, c_ref, s_ref = _quant_check(w, "row magnitudes")
+    say(f"mxfp4_gemv row magnitudes n={n} k={k} b={b}")
+    y = host(bg.mxfp4_gemv(dev_bf16(x), mw)).astype(np.float64)
+    y_ref = oracle.mx_matmul(x, c_ref, s_ref, n, k)
+    from workloads import bf16_bits_to_f32
+    bound = np.abs(bf16_bits_to_f32(x).astype(np.float64)) @ np.abs(oracle.mx_dequantize(c_ref, s_ref, n, k)).T
+    err = np.abs(y - y_ref)
+    worst = float(np.max(err / np.where(bound > 0, bound, 1.0)))
+    say(f"  worst |y - y_ref| / sum|x w| = {worst:.2e}")
+    assert np.all(np.isfinite(y))
+    assert np.all(err <= 1e-4 * bound), worst
