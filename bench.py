@@ -404,6 +404,21 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_kt -o kt
 PMC_CMD = "rocprofv3 --pmc {c} -d $REPO/gpurun_out/prof_{d} -o {d} -- python3 $REPO/bench.py --counter-pass"
 
 
+def _kernel_short_name(name: str) -> str:
+    """Kernel name without its argument list, keeping template arguments
+    that contain parentheses, e.g. (lq::WeightFormat)0."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
 def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
     """Write profiles/*.md and the counter JSON from three rocprofv3 databases."""
     import sqlite3
@@ -422,7 +437,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
              "| kernel | grid | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
     dom_avg = None
     for name, cnt, avg, mn, mx, tot, gx in rows:
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        short = _kernel_short_name(name)
         if len(short) > 70:
             short = short[:67] + "..."
         lines.append(f"| `{short}` | {gx} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e6:.3f} |")
