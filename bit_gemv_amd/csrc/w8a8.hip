@@ -9,15 +9,16 @@
 //   y[m][n]   = ((float) acc[m][n] * sx[m]) * sw[n]
 // Both operands are K-contiguous, so a lane's 16-byte slice of a row is an
 // MFMA operand fragment. A block of 4 waves computes 128 x 128 outputs (2 x 2
-// waves of 64 x 64 = 4 x 4 tiles of 16 x 16) and walks k in 64-wide steps.
-// The step's 128 x 64 slices of qx and qw go straight from memory into LDS
-// (buffer loads with the LDS-write form, 16 bytes a lane), into a ring of
-// kStages slots filled kStages - 1 steps ahead, so one wave per SIMD keeps
-// several steps of loads in flight while its MFMAs run. No VGPRs hold
+// waves of 64 x 64 = 4 x 4 tiles of 16 x 16) and walks k in 128-wide steps
+// (32 MFMAs per wave between two barriers; 64-wide steps measured 3-26 %
+// slower). The step's 128 x 128 slices of qx and qw go straight from memory
+// into LDS (buffer loads with the LDS-write form, 16 bytes a lane), into a
+// ring of kStages slots filled kStages - 1 steps ahead, so one wave per SIMD
+// keeps several steps of loads in flight while its MFMAs run. No VGPRs hold
 // staged data.
-// LDS slot layout: 128 rows of 64 bytes per operand; the four 16-byte chunks
-// of row r are stored XOR-permuted by swz(r) so that the 16 rows read by one
-// fragment load hit distinct banks.
+// LDS slot layout: 128 rows of 128 bytes per operand; the eight 16-byte
+// chunks of row r are stored XOR-permuted by swz(r) = (r >> 1) & 7, so the 16
+// rows read by one fragment load hit distinct banks.
 // Blocks are mapped XCD-aware: the hardware deals block b to XCD b % 8, and
 // the blocks that share a 128-row slice of qw are put on one XCD so the
 // slice is fetched into that XCD's L2 once.
@@ -30,15 +31,15 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kStages = 6;                      // LDS ring depth
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int kStages = 4;                      // LDS ring depth (128 KB)
 constexpr int kSlot = (BM + BN) * BK;           // bytes of one ring slot (qx rows, then qw rows)
 constexpr int kLoadsPerStep = kSlot / 1024 / 4; // 1 KB loads per wave per step
 // vmcnt limits (literals: they are pasted into the step barrier's asm)
 #define kVmPrologue 16  // (kStages - 2) steps of loads may stay pending
-#define kVmStep 12      // (kStages - 3) steps
+#define kVmStep 8       // (kStages - 3) steps
 
-LQ_DEVICE int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+LQ_DEVICE int swz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt immediate (gfx9 layout): vmcnt(0), expcnt and lgkmcnt not waited on
 constexpr int kWaitVm0 = 0x0F70;
@@ -76,16 +77,16 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
     const auto ra = make_rsrc(qx + (int64_t)m0 * k, (uint32_t)rows_m * (uint32_t)k);
     const auto rb = make_rsrc(qw + (int64_t)n0 * k, (uint32_t)rows_n * (uint32_t)k);
 
-    // This wave's loads: 1 KB pieces q = 4 wave + i (i < 4) of a slot; piece
-    // q < 8 covers qx rows 16 q .. + 15, piece q >= 8 qw rows 16 (q - 8) ...
-    // Lane l writes LDS bytes 16 l of the piece: row 16 q' + l / 4, chunk
-    // slot l % 4, which holds the row's logical chunk (l % 4) ^ swz(row).
+    // This wave's loads: 1 KB pieces q = 8 wave + i (i < 8) of a slot; piece
+    // q < 16 covers qx rows 8 q .. + 7, piece q >= 16 qw rows 8 (q - 16) ...
+    // Lane l writes LDS bytes 16 l of the piece: row 8 q' + l / 8, chunk
+    // slot l % 8, which holds the row's logical chunk (l % 8) ^ swz(row).
     uint32_t src_off[kLoadsPerStep];
 #pragma unroll
     for (int i = 0; i < kLoadsPerStep; ++i) {
-        const int q = 4 * wave + i;
-        const int row = 16 * (q & 7) + (lane >> 2);
-        src_off[i] = (uint32_t)row * (uint32_t)k + 16u * (uint32_t)((lane & 3) ^ swz(row));
+        const int q = kLoadsPerStep * wave + i;
+        const int row = 8 * (q & 15) + (lane >> 3);
+        src_off[i] = (uint32_t)row * (uint32_t)k + 16u * (uint32_t)((lane & 7) ^ swz(row));
     }
     const int nsteps = k / BK;
     auto issue = [&](int ks) {
@@ -98,13 +99,13 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
 #pragma unroll
             for (int i = 0; i < kLoadsPerStep; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ra, (__attribute__((address_space(3))) void *)(slot + 1024 * (4 * wave + i)), 16,
+                    ra, (__attribute__((address_space(3))) void *)(slot + 1024 * (kLoadsPerStep * wave + i)), 16,
                     in ? src_off[i] + (uint32_t)ks * BK : kOutOfRange, 0, 0, 0);
         } else {
 #pragma unroll
             for (int i = 0; i < kLoadsPerStep; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rb, (__attribute__((address_space(3))) void *)(slot + 1024 * (4 * wave + i)), 16,
+                    rb, (__attribute__((address_space(3))) void *)(slot + 1024 * (kLoadsPerStep * wave + i)), 16,
                     in ? src_off[i] + (uint32_t)ks * BK : kOutOfRange, 0, 0, 0);
         }
     };
@@ -115,14 +116,17 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    // fragment addresses within a slot: lane (row l16, k quarter kq)
-    int a_off[4], b_off[4];
+    // fragment addresses within a slot: lane (row l16, k quarter kq) of the
+    // step's half h (64 k each)
+    int a_off[2][4], b_off[2][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int ra_row = wm * 64 + t * 16 + l16, rb_row = wn * 64 + t * 16 + l16;
-        a_off[t] = ra_row * BK + 16 * (kq ^ swz(ra_row));
-        b_off[t] = BM * BK + rb_row * BK + 16 * (kq ^ swz(rb_row));
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int ra_row = wm * 64 + t * 16 + l16, rb_row = wn * 64 + t * 16 + l16;
+            a_off[h][t] = ra_row * BK + 16 * ((4 * h + kq) ^ swz(ra_row));
+            b_off[h][t] = BM * BK + rb_row * BK + 16 * ((4 * h + kq) ^ swz(rb_row));
+        }
 
     // The row and column scales of this lane's outputs, loaded up front
     // (rows past m and columns past n read zeros): the epilogue's stores then
@@ -144,17 +148,21 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
     auto read_frags = [&](int ks, i32x4 *af, i32x4 *bf) {
         const int8_t *slot = ring[ks % kStages];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            af[t] = *reinterpret_cast<const i32x4 *>(slot + a_off[t]);
-            bf[t] = *reinterpret_cast<const i32x4 *>(slot + b_off[t]);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                af[4 * h + t] = *reinterpret_cast<const i32x4 *>(slot + a_off[h][t]);
+                bf[4 * h + t] = *reinterpret_cast<const i32x4 *>(slot + b_off[h][t]);
+            }
     };
     auto mfmas = [&](const i32x4 *af, const i32x4 *bf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[4 * h + i], bf[4 * h + j], acc[i][j], 0, 0, 0);
     };
     // Step barrier. LDS-write loads are counted by vmcnt only and the
     // compiler does not track them, so the waits are explicit: a wave's own
@@ -171,10 +179,12 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const int8_t *__restrict__ qx
     // (read during step ks - 2) the step's load then refills.
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) issue(s);
-    i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+    // With an odd step count the last iteration's second half computes the
+    // step past the end, whose slot the out-of-range loads filled with zeros.
+    i32x4 fa0[8], fb0[8], fa1[8], fb1[8];
     LQ_STEP_SYNC(kVmPrologue);
     read_frags(0, fa0, fb0);
-    for (int ks = 0; ks < nsteps; ks += 2) {  // nsteps is even: k is a multiple of 128
+    for (int ks = 0; ks < nsteps; ks += 2) {
         LQ_STEP_SYNC(kVmStep);
         issue(ks + kStages - 1);
         read_frags(ks + 1, fa1, fb1);
