@@ -34,45 +34,67 @@ LQ_DEVICE int mx_exponent(float amax) {
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Nearest E2M1 magnitude index of a in [0, 6]; at a tie the neighbour with
-// the even encoding wins (midpoints 0.25, 1.25, 2.5, 5 stay down, 0.75,
-// 1.75, 3.5 go up).
-LQ_DEVICE uint32_t e2m1_index(float a) {
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-           (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Codes of 8 elements (one 16-byte chunk of bf16) with the block exponent e:
+// element j's nibble at bits 4j..4j+3. v_cvt_scalef32_pk_fp4_bf16 computes
+// x / 2^e rounded to the nearest E2M1 value, ties to the even encoding, for
+// two bf16 at a time -- the rounding read from the pages, checked on the
+// device for every finite bf16 value at scales 2^-127 .. 2^127. The scale
+// operand is the E8M0 byte in the fp32 exponent field (the byte 0, 0.0f,
+// acts as 2^-127). The conversion keeps the sign of a value that rounds to
+// magnitude 0 (code 8, -0); such codes are turned into +0 afterwards.
+LQ_DEVICE uint32_t e2m1_codes8(const u32x4 v, int e) {
+    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+    // each pair into byte 0 of a zero word (the form checked on the device),
+    // then shifted into place. (The words are copied out of the vector
+    // first: a bit-cast of a vector element itself read element 0.)
+    const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2_t pair = __builtin_bit_cast(bf16x2_t, words[i]);
+        c |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, pair, scale, 0) & 0xFFu) << (8 * i);
+    }
+    // keep the sign bit of a nibble only where its magnitude is nonzero
+    const uint32_t mag = c & 0x77777777u;
+    const uint32_t nz = (mag | (mag >> 1) | (mag >> 2)) & 0x11111111u;
+    return mag | (c & (nz << 3));
 }
 
-LQ_DEVICE uint32_t e2m1_code(float x, int e) {
-    const float v = __builtin_amdgcn_ldexpf(x, -e);  // exact unless below the fp32 normal range (then 0)
-    const uint32_t mag = e2m1_index(fabsf(v));
-    return mag == 0 ? 0u : (mag | (x < 0.0f ? 8u : 0u));
-}
+// A lane quantizes kMxChunks chunks of 8 elements (16 bytes of bf16), all
+// loads issued first; 4 consecutive lanes of a chunk slice form a block of
+// 32 and share its maximum through two DPP steps. The matrix is flattened:
+// k is a multiple of 32, so blocks never span rows and block b covers
+// elements [32 b, 32 b + 32), code bytes [16 b, 16 b + 16) and scale byte b.
+constexpr int kMxChunks = 4;
 
-// One lane quantizes 8 elements (16 bytes of bf16); 4 lanes form a block of
-// 32. The matrix is flattened: k is a multiple of 32, so blocks never span
-// rows and block b covers elements [32 b, 32 b + 32), code bytes
-// [16 b, 16 b + 16) and scale byte b.
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restrict__ w, int64_t total8,
                                                        uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    // lanes past the end take part in the 4-lane maximum with zeros
-    const bool in = i < total8;
-    const u32x4 v = in ? reinterpret_cast<const u32x4 *>(w)[i] : u32x4{0u, 0u, 0u, 0u};
-    float xs[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                   bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    float a = 0.0f;
+    const int64_t base = (int64_t)blockIdx.x * (256 * kMxChunks) + threadIdx.x;
+    u32x4 v[kMxChunks];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(xs[j]));
-    // maximum over the block's 4 lanes (aligned quads of the wave)
-    a = fmaxf(a, dpp_move<kDppXor1>(a));
-    a = fmaxf(a, dpp_move<kDppXor2>(a));
-    const int e = mx_exponent(a);
-    uint32_t packed = 0;
+    for (int c = 0; c < kMxChunks; ++c) {
+        const int64_t i = base + 256 * c;
+        // lanes past the end take part in the 4-lane maximum with zeros
+        v[c] = i < total8 ? reinterpret_cast<const u32x4 *>(w)[i] : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) packed |= e2m1_code(xs[j], e) << (4 * j);
-    if (in) {
-        reinterpret_cast<uint32_t *>(codes)[i] = packed;
-        if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+    for (int c = 0; c < kMxChunks; ++c) {
+        const int64_t i = base + 256 * c;
+        const uint32_t words[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(words[j])), fabsf(bf16_hi(words[j]))));
+        // maximum over the block's 4 lanes (aligned quads of the wave)
+        a = fmaxf(a, dpp_move<kDppXor1>(a));
+        a = fmaxf(a, dpp_move<kDppXor2>(a));
+        const int e = mx_exponent(a);
+        const uint32_t packed = e2m1_codes8(v[c], e);
+        if (i < total8) {
+            reinterpret_cast<uint32_t *>(codes)[i] = packed;
+            if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+        }
     }
 }
 
@@ -238,8 +260,8 @@ hipError_t launch_mx(const MxArgs &a, hipStream_t st) {
 hipError_t launch_mx_quantize(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales,
                               hipStream_t st) {
     const int64_t total8 = n * k / 8;
-    hipLaunchKernelGGL(mx_quant_kernel, dim3((uint32_t)((total8 + 255) / 256)), dim3(256), 0, st, w, total8, codes,
-                       scales);
+    hipLaunchKernelGGL(mx_quant_kernel, dim3((uint32_t)((total8 + 256 * kMxChunks - 1) / (256 * kMxChunks))), dim3(256),
+                       0, st, w, total8, codes, scales);
     return hipGetLastError();
 }
 
