@@ -273,8 +273,9 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
 
         ms = _timed(factor, reps=2)
         us[kk] = out["u"]
-        # H on bf16 MFMA (2 t k^2), reverse Cholesky and inverse (about 2 k^3 / 3 each)
-        fl = 2.0 * aw.tokens * kk * kk + 4.0 * kk ** 3 / 3
+        # minimal flop counts: X^T X as a symmetric rank-t update (t k^2), the
+        # Cholesky factor (k^3 / 3) and the triangular inverse (k^3 / 3)
+        fl = 1.0 * aw.tokens * kk * kk + 2.0 * kk ** 3 / 3
         fl_fac += fl
         t_fac += ms
         gq[f"factor k={kk}"] = {"ms": round(ms, 3), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}

@@ -29,6 +29,8 @@
 //    whose accumulator starts at W and adds the block's terms in column
 //    order with fused multiply-adds -- the same operations, in the same
 //    order, as applying each column's update as it is made.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -113,6 +115,145 @@ hipError_t sgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int
     return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// fp32 GEMM on the matrix cores (v_mfma_f32_16x16x4f32) for the factor, where
+// only fp32 accuracy matters (the column loop keeps the GEMM above, whose
+// fixed accumulation order its codes depend on):
+//   C[M][N] = (beta ? C : 0) + sgn * A[M][K] op(B),
+// op(B) = B[K][N] (BT = false) or B^T with B given [N][K] (BT = true). M, N
+// and K are multiples of 64 (the factor's panels). UPPER: only the 64 x 64
+// output tiles on or above the block diagonal are computed (the trailing
+// update keeps the upper triangle of H, the only part read later). AUPPER:
+// A is upper triangular, so row block i0 starts its sum at k = i0. PARTIAL:
+// blockIdx.z takes the k range [z ksplit, (z + 1) ksplit) and writes its
+// partial sum to C + z M N (ld N, no beta); sum_splits_kernel adds the
+// partials in z order, so the result does not depend on scheduling.
+// Block: 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA tiles); k in steps
+// of 16 through LDS, the next step's loads in registers during the current
+// step's MFMAs. MFMA operands: lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16] of a 16 x 16 x 4 step, and D rows 4 (l / 16) + v of
+// column l % 16.
+// --------------------------------------------------------------------------
+template <bool BT, bool UPPER, bool AUPPER, bool PARTIAL>
+__global__ __launch_bounds__(256) void mgemm_kernel(int M, int N, int K, float sgn, const float *A, int64_t lda,
+                                                    const float *B, int64_t ldb, int beta, float *C, int64_t ldc,
+                                                    int ksplit) {
+    // A tile [64 rows][16 k] at a row stride of 20 floats (16-byte aligned
+    // rows, conflict-free fragment reads); B tile likewise when BT, else
+    // [16 k][64 n] at a stride of 80 floats
+    __shared__ __attribute__((aligned(16))) float As[64 * 20];
+    __shared__ __attribute__((aligned(16))) float Bs[BT ? 64 * 20 : 16 * 80];
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    if (UPPER && i0 > j0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int kb = max(AUPPER ? i0 : 0, PARTIAL ? (int)blockIdx.z * ksplit : 0);
+    const int ke = PARTIAL ? min(K, ((int)blockIdx.z + 1) * ksplit) : K;
+    if (PARTIAL) C += (int64_t)blockIdx.z * M * ldc;
+    // this thread's 16-byte loads: A row tid / 4, k 4 (tid % 4); B the same
+    // (BT) or k row tid / 16, n 4 (tid % 16)
+    const int ar = tid >> 2, ak = 4 * (tid & 3);
+    const int br = BT ? tid >> 2 : tid >> 4, bc = BT ? 4 * (tid & 3) : 4 * (tid & 15);
+    const float *ap = A + (int64_t)(i0 + ar) * lda + ak;
+    const float *bp = BT ? B + (int64_t)(j0 + br) * ldb + bc : B + (int64_t)br * ldb + j0 + bc;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[mt][nt][v] = beta && !PARTIAL
+                                     ? C[(int64_t)(i0 + wm * 32 + mt * 16 + 4 * lq + v) * ldc + j0 + wn * 32 + nt * 16 + l16]
+                                     : 0.0f;
+    // an empty k range (a split wholly below a triangular A's row block)
+    // still writes its zero partial
+    f32x4 ra = f32x4{0.f, 0.f, 0.f, 0.f}, rb = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb < ke) {
+        ra = *reinterpret_cast<const f32x4 *>(ap + kb);
+        rb = BT ? *reinterpret_cast<const f32x4 *>(bp + kb) : *reinterpret_cast<const f32x4 *>(bp + (int64_t)kb * ldb);
+    }
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+        *reinterpret_cast<f32x4 *>(&As[ar * 20 + ak]) = ra;
+        if (BT)
+            *reinterpret_cast<f32x4 *>(&Bs[br * 20 + bc]) = rb;
+        else
+            *reinterpret_cast<f32x4 *>(&Bs[br * 80 + bc]) = rb;
+        __syncthreads();
+        if (k0 + 16 < ke) {
+            ra = *reinterpret_cast<const f32x4 *>(ap + k0 + 16);
+            rb = BT ? *reinterpret_cast<const f32x4 *>(bp + k0 + 16)
+                    : *reinterpret_cast<const f32x4 *>(bp + (int64_t)(k0 + 16) * ldb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4) {
+            float a[2], b[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) a[mt] = sgn * As[(wm * 32 + mt * 16 + l16) * 20 + kk + lq];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                b[nt] = BT ? Bs[(wn * 32 + nt * 16 + l16) * 20 + kk + lq] : Bs[(kk + lq) * 80 + wn * 32 + nt * 16 + l16];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                C[(int64_t)(i0 + wm * 32 + mt * 16 + 4 * lq + v) * ldc + j0 + wn * 32 + nt * 16 + l16] = acc[mt][nt][v];
+}
+
+template <bool BT, bool UPPER, bool AUPPER>
+hipError_t mgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B, int64_t ldb,
+                 int beta, float *C, int64_t ldc, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (M % 64 || N % 64 || K % 64) return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)(N / 64), (uint32_t)(M / 64));
+    hipLaunchKernelGGL((mgemm_kernel<BT, UPPER, AUPPER, false>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn,
+                       A, lda, B, ldb, beta, C, ldc, 0);
+    return hipGetLastError();
+}
+
+// C[i][j] = sum over z of part[z][i][j], z in order
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits, int M, int N,
+                                                         float *__restrict__ C, int64_t ldc) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)M * N) return;
+    const int i = (int)(e / N), j = (int)(e % N);
+    float v = 0.0f;
+    for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + e];
+    C[(int64_t)i * ldc + j] = v;
+}
+
+constexpr int kMaxSplits = 16;  // k ranges of the narrow, deep products
+
+// A narrow product (N = 64) with a deep k: k split into up to kMaxSplits
+// ranges of at least 1024 so that enough workgroups run; the partials go to
+// part (kMaxSplits M N floats) and are summed in order.
+template <bool BT, bool AUPPER>
+hipError_t mgemm_deep(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B,
+                      int64_t ldb, float *C, int64_t ldc, float *part, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (M % 64 || N % 64 || K % 64) return hipErrorInvalidValue;
+    const int splits = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, K / 1024));
+    if (splits == 1) return mgemm<BT, false, AUPPER>(M, N, K, sgn, A, lda, B, ldb, 0, C, ldc, st);
+    const int64_t ksplit = (K / 64 + splits - 1) / splits * 64;
+    const dim3 grid((uint32_t)(N / 64), (uint32_t)(M / 64), (uint32_t)splits);
+    hipLaunchKernelGGL((mgemm_kernel<BT, false, AUPPER, true>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn, A,
+                       lda, B, ldb, 0, part, N, (int)ksplit);
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((uint32_t)((M * N + 255) / 256)), dim3(256), 0, st, part, splits, (int)M,
+                       (int)N, C, ldc);
+    return hipGetLastError();
+}
+
 // X [t][k] bf16 -> X^T [k][tp] bf16, tokens t .. tp - 1 zero (tp a multiple of 64).
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ x, int t, int k, int tp,
                                                              uint16_t *__restrict__ xt) {
@@ -159,44 +300,73 @@ constexpr int NB = 64;  // panel width of the factorisation
 
 // The diagonal block B = [j0, j0 + 64) of the (updated) H: reverse Cholesky
 // V_BB (H_BB = V_BB V_BB^T, upper) written back into H's block, and its
-// inverse into vinv (64 x 64, zeros below the diagonal). One workgroup.
+// inverse into vinv (64 x 64, zeros below the diagonal). One workgroup; both
+// steps are right-looking with one barrier per step: a step reads the
+// column (row) it finalises unscaled, writes the finished values to a
+// separate array, and updates the part still to be processed:
+//  * Cholesky, column j from the last, on the working block A (= H_BB):
+//    F_ij = A_ij / sqrt(A_jj) (i < j), F_jj = sqrt(A_jj), and
+//    A_il -= A_ij A_lj / A_jj for i, l < j (kept symmetric);
+//  * inverse W = F^-1 from W = I, row m from the last: the final row is
+//    W_m. / F_mm, and W_i. -= (F_im / F_mm) W_m. for i < m.
 __global__ __launch_bounds__(256) void chol_diag_kernel(float *__restrict__ h, int k, int j0,
                                                         float *__restrict__ vinv) {
-    __shared__ float V[NB][NB + 1];
+    __shared__ float A[NB][NB + 1];
+    __shared__ float F[NB][NB + 1];
     __shared__ float W[NB][NB + 1];
     const int tid = threadIdx.x;
-    for (int e = tid; e < NB * NB; e += 256) V[e / NB][e % NB] = h[(int64_t)(j0 + e / NB) * k + j0 + e % NB];
+    const int c = tid & 63, r0 = tid >> 6;  // column of this thread; rows r0, r0 + 4, ...
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int i = e / NB, l = e % NB;
+        // the block's upper triangle is current; mirror it (H is symmetric)
+        A[i][l] = i <= l ? h[(int64_t)(j0 + i) * k + j0 + l] : h[(int64_t)(j0 + l) * k + j0 + i];
+        F[i][l] = 0.0f;
+        W[i][l] = i == l ? 1.0f : 0.0f;
+    }
     __syncthreads();
     for (int j = NB - 1; j >= 0; --j) {
-        if (tid == 0) {
-            float d = V[j][j];
-            for (int c = j + 1; c < NB; ++c) d -= V[j][c] * V[j][c];
-            V[j][j] = sqrtf(d);  // not positive definite: NaN, which propagates to U
-        }
-        __syncthreads();
-        if (tid < j) {
-            float s = V[tid][j];
-            for (int c = j + 1; c < NB; ++c) s -= V[tid][c] * V[j][c];
-            V[tid][j] = s / V[j][j];
+        // hardware 1 / sqrt (about 1 ulp; the factor needs fp32 accuracy,
+        // not correct rounding); not positive definite: NaN or inf, which
+        // propagates to U
+        const float ajj = A[j][j];
+        const float rs = __builtin_amdgcn_rsqf(ajj);
+        if (tid < j) F[tid][j] = A[tid][j] * rs;
+        if (tid == j) F[j][j] = ajj * rs;
+        if (c < j) {
+            // all 32 reads first (the column and this thread's 16 rows), then
+            // the updates: one LDS round trip instead of one per row. Rows
+            // i >= j are updated too, unconditionally: they are finished
+            // and never read again, and the stores need no branches.
+            const float alj = A[c][j] * (rs * rs);
+            float aij[NB / 4], aic[NB / 4];
+#pragma unroll
+            for (int t = 0; t < NB / 4; ++t) {
+                aij[t] = A[r0 + 4 * t][j];
+                aic[t] = A[r0 + 4 * t][c];
+            }
+#pragma unroll
+            for (int t = 0; t < NB / 4; ++t) A[r0 + 4 * t][c] = __builtin_fmaf(-aij[t], alj, aic[t]);
         }
         __syncthreads();
     }
-    // W = V^-1 (upper): thread c solves column c by back substitution
-    if (tid < NB) {
-        const int c = tid;
-        for (int i = 0; i < NB; ++i) W[i][c] = 0.0f;
-        W[c][c] = 1.0f / V[c][c];
-        for (int i = c - 1; i >= 0; --i) {
-            float s = 0.0f;
-            for (int m = i + 1; m <= c; ++m) s += V[i][m] * W[m][c];
-            W[i][c] = -s / V[i][i];
+    for (int m = NB - 1; m >= 0; --m) {
+        const float wmc = W[m][c] * __builtin_amdgcn_rcpf(F[m][m]);
+        if (tid < NB) vinv[m * NB + c] = c >= m ? wmc : 0.0f;
+        // every row is updated: F is zero below the diagonal, and rows
+        // i >= m are finished and not read again
+        float fim[NB / 4], wic[NB / 4];
+#pragma unroll
+        for (int t = 0; t < NB / 4; ++t) {
+            fim[t] = F[r0 + 4 * t][m];
+            wic[t] = W[r0 + 4 * t][c];
         }
+#pragma unroll
+        for (int t = 0; t < NB / 4; ++t) W[r0 + 4 * t][c] = __builtin_fmaf(-fim[t], wmc, wic[t]);
+        __syncthreads();
     }
-    __syncthreads();
     for (int e = tid; e < NB * NB; e += 256) {
-        const int i = e / NB, c = e % NB;
-        if (i <= c) h[(int64_t)(j0 + i) * k + j0 + c] = V[i][c];
-        vinv[e] = i <= c ? W[i][c] : 0.0f;
+        const int i = e / NB, l = e % NB;
+        if (i <= l) h[(int64_t)(j0 + i) * k + j0 + l] = F[i][l];
     }
 }
 
@@ -321,7 +491,8 @@ constexpr int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 int64_t gptq_factor_workspace_bytes(int64_t t, int64_t k) {
     const int64_t tp = (t + 63) / 64 * 64;
-    return align256(k * tp * 2) + align256(k * k * 4) + align256(k * NB * 4) + align256(k * NB * 4) + 256;
+    return align256(k * tp * 2) + align256(k * k * 4) + align256(k * NB * 4) + align256(k * NB * 4) + 256 +
+           align256(kMaxSplits * k * NB * 4);
 }
 
 int64_t gptq_quantize_workspace_bytes(int64_t n, int64_t k) { return align256(n * k * 4) + align256(n * GB * 4); }
@@ -339,6 +510,8 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
     float *tmp = reinterpret_cast<float *>(ws);  // [k][64]
     ws += align256(k * NB * 4);
     double *dsum = reinterpret_cast<double *>(ws);
+    ws += 256;
+    float *part = reinterpret_cast<float *>(ws);  // [kMaxSplits][k][64]
     hipError_t e;
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((uint32_t)((k + 31) / 32), (uint32_t)(tp / 32)), dim3(256), 0, st,
                        x, (int)t, (int)k, (int)tp, xt);
@@ -354,10 +527,13 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, h, (int)k, (int)j0, vinv + p * NB * NB);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (j0 == 0) continue;
-        // V_AB = H_AB Vinv_BB^T (in place), then H_AA -= V_AB V_AB^T
-        if ((e = sgemm<true>(j0, NB, NB, 1.0f, h + j0, k, vinv + p * NB * NB, NB, 0, h + j0, k, st)) != hipSuccess)
+        // V_AB = H_AB Vinv_BB^T (in place: each workgroup owns 64 rows and
+        // reads all of them before it writes), then the upper triangle of
+        // H_AA -= V_AB V_AB^T
+        if ((e = mgemm<true, false, false>(j0, NB, NB, 1.0f, h + j0, k, vinv + p * NB * NB, NB, 0, h + j0, k, st)) !=
+            hipSuccess)
             return e;
-        if ((e = sgemm<true>(j0, j0, NB, -1.0f, h + j0, k, h + j0, k, 1, h, k, st)) != hipSuccess) return e;
+        if ((e = mgemm<true, true, false>(j0, j0, NB, -1.0f, h + j0, k, h + j0, k, 1, h, k, st)) != hipSuccess) return e;
     }
     // U = V^-1, first panel first: U_BB = Vinv_BB, U_AB = -U_AA (V_AB U_BB)
     hipLaunchKernelGGL(fill_kernel, dim3(2048), dim3(256), 0, st, u, k * k);
@@ -367,9 +543,11 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
         hipLaunchKernelGGL(put_block_kernel, dim3(1), dim3(256), 0, st, vinv + p * NB * NB, u, (int)k, (int)j0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (j0 == 0) continue;
-        if ((e = sgemm<false>(j0, NB, NB, 1.0f, h + j0, k, u + j0 * k + j0, k, 0, tmp, NB, st)) != hipSuccess)
+        if ((e = mgemm<false, false, false>(j0, NB, NB, 1.0f, h + j0, k, u + j0 * k + j0, k, 0, tmp, NB, st)) !=
+            hipSuccess)
             return e;
-        if ((e = sgemm<false>(j0, NB, j0, -1.0f, u, k, tmp, NB, 0, u + j0, k, st)) != hipSuccess) return e;
+        // U_AA is upper triangular: row block i0 sums from k = i0
+        if ((e = mgemm_deep<false, true>(j0, NB, j0, -1.0f, u, k, tmp, NB, u + j0, k, part, st)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
