@@ -21,7 +21,7 @@
 //              X' = bf16(X / s)                        (div_act_kernel)
 //              quant(W diag(s))                        (the group-wise quantizer)
 //              Y' = X' W_hat'^T                        (the W4A16 GEMM)
-//              loss = sum (Y - Y')^2                   (sqerr kernels, fp64)
+//              loss = sum (Y - Y')^2                   (in the GEMM's epilogue, fp64)
 //   then:      argmin, s_best, quant(W diag(s_best))   (awq_pick_kernel + quantizer)
 // Channel magnitudes s_X come from act_absmean_kernel (a separate entry
 // point, so the caller can reuse them across the layer's linears).
@@ -64,10 +64,11 @@ LQ_DEVICE float awq_scale_of(float sxj, int i, int n_grid) {
     return powf(sxj < kFloor ? kFloor : sxj, alpha);
 }
 
-__global__ __launch_bounds__(256) void awq_scale_kernel(const float *__restrict__ sx, int k, int i, int n_grid,
-                                                        float *__restrict__ s) {
+// Grid point i0 + blockIdx.y; its scales at s + blockIdx.y * s_stride.
+__global__ __launch_bounds__(256) void awq_scale_kernel(const float *__restrict__ sx, int k, int i0, int n_grid,
+                                                        float *__restrict__ s, int64_t s_stride) {
     const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j < k) s[j] = awq_scale_of(sx[j], i, n_grid);
+    if (j < k) s[blockIdx.y * s_stride + j] = awq_scale_of(sx[j], i0 + (int)blockIdx.y, n_grid);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite values).
@@ -78,8 +79,12 @@ LQ_DEVICE uint32_t bf16_rne(float f) {
 
 // X'[t][j] = bf16(X[t][j] / s[j]) (IEEE division). One thread per 8
 // consecutive activations (one 16-byte load and store); k is a multiple of 8.
+// Grid point blockIdx.y: s and X' at blockIdx.y times their strides.
 __global__ __launch_bounds__(256) void div_act_kernel(const uint16_t *__restrict__ x, int64_t total8, int k,
-                                                      const float *__restrict__ s, uint16_t *__restrict__ xa) {
+                                                      const float *__restrict__ s, int64_t s_stride,
+                                                      uint16_t *__restrict__ xa, int64_t x_stride) {
+    s += blockIdx.y * s_stride;
+    xa += blockIdx.y * x_stride;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total8; i += (int64_t)gridDim.x * 256) {
         const u32x4 v = reinterpret_cast<const u32x4 *>(x)[i];
         const int j0 = (int)((i * 8) % k);
@@ -98,8 +103,6 @@ __global__ __launch_bounds__(256) void div_act_kernel(const uint16_t *__restrict
 // Squared error sum((Y - Y')^2) in fp64: per-block partials over a fixed
 // grid-stride assignment, then one block adds them in a fixed order.
 // --------------------------------------------------------------------------
-constexpr int kSqBlocks = 512;
-
 LQ_DEVICE double block_sum(double v, double *lds) {
     // 256 threads: tree through LDS in a fixed order
     lds[threadIdx.x] = v;
@@ -109,38 +112,6 @@ LQ_DEVICE double block_sum(double v, double *lds) {
         __syncthreads();
     }
     return lds[0];
-}
-
-__global__ __launch_bounds__(256) void sqerr_partial_kernel(const float *__restrict__ a, const float *__restrict__ b,
-                                                            int64_t total, double *__restrict__ partials) {
-    __shared__ double lds[256];
-    double acc = 0.0;
-    const int64_t total4 = total / 4;
-    // the last total % 4 elements: block 0
-    if (blockIdx.x == 0 && (int64_t)threadIdx.x < total - 4 * total4) {
-        const double d = (double)a[4 * total4 + threadIdx.x] - (double)b[4 * total4 + threadIdx.x];
-        acc = d * d;
-    }
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (int64_t)kSqBlocks * 256) {
-        const f32x4 u = reinterpret_cast<const f32x4 *>(a)[i];
-        const f32x4 v = reinterpret_cast<const f32x4 *>(b)[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const double d = (double)u[e] - (double)v[e];
-            acc = __builtin_fma(d, d, acc);
-        }
-    }
-    const double s = block_sum(acc, lds);
-    if (threadIdx.x == 0) partials[blockIdx.x] = s;
-}
-
-__global__ __launch_bounds__(256) void sqerr_finish_kernel(const double *__restrict__ partials,
-                                                           double *__restrict__ out) {
-    __shared__ double lds[256];
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < kSqBlocks; i += 256) acc += partials[i];
-    const double s = block_sum(acc, lds);
-    if (threadIdx.x == 0) *out = s;
 }
 
 // Argmin over the grid (first minimum), then s_best and the index.
@@ -290,8 +261,18 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int
     return hipGetLastError();
 }
 
+// Grid points evaluated per batch: their quantized weights and scaled
+// activations sit side by side in the workspace, and one launch of the
+// W4A16 GEMM computes all their products with the squared error against
+// the reference product fused into its epilogue (at n = 4096 one product
+// alone is only 128 workgroups).
+constexpr int kAwqBatch = 4;
+
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
-    return 2 * align256(t * n * 4) + align256(t * k * 2) + align256(k * 4) + align256(kSqBlocks * 8);
+    const int64_t meta = n * (k / 128) * 4;  // scales (or zeros) of one point, group >= 128
+    return align256(t * n * 4) + kAwqBatch * (align256(t * k * 2) + align256(k * 4) + align256(n * k / 2) +
+                                              2 * align256(meta)) +
+           align256(kAwqBatch * w4a16_gemm_blocks(t, n) * 8);
 }
 
 hipError_t launch_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx, hipStream_t st) {
@@ -299,17 +280,38 @@ hipError_t launch_act_absmean(const uint16_t *x, int64_t t, int64_t k, float *sx
     return hipGetLastError();
 }
 
+// The loss of grid point z: the workgroup partials of its product, summed
+// in a fixed order.
+__global__ __launch_bounds__(256) void loss_finish_kernel(const double *__restrict__ partials, int64_t blocks,
+                                                          double *__restrict__ out) {
+    __shared__ double lds[256];
+    const double *p = partials + (int64_t)blockIdx.x * blocks;
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < blocks; i += 256) acc += p[i];
+    const double s = block_sum(acc, lds);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
 hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st) {
+    const int64_t meta = a.n * (a.k / 128) * 4;
     uint8_t *ws = static_cast<uint8_t *>(a.workspace);
     float *y_ref = reinterpret_cast<float *>(ws);
     ws += align256(a.t * a.n * 4);
-    float *y_q = reinterpret_cast<float *>(ws);
-    ws += align256(a.t * a.n * 4);
-    uint16_t *xa = reinterpret_cast<uint16_t *>(ws);
-    ws += align256(a.t * a.k * 2);
-    float *s = reinterpret_cast<float *>(ws);
-    ws += align256(a.k * 4);
-    double *partials = reinterpret_cast<double *>(ws);
+    uint16_t *xa = reinterpret_cast<uint16_t *>(ws);  // [kAwqBatch][t][k]
+    ws += kAwqBatch * align256(a.t * a.k * 2);
+    float *s = reinterpret_cast<float *>(ws);  // [kAwqBatch][k]
+    ws += kAwqBatch * align256(a.k * 4);
+    uint8_t *codes = ws;  // [kAwqBatch][n][k / 2]
+    ws += kAwqBatch * align256(a.n * a.k / 2);
+    float *scales = reinterpret_cast<float *>(ws);  // [kAwqBatch][n][k / group]
+    ws += kAwqBatch * align256(meta);
+    float *zeros = reinterpret_cast<float *>(ws);
+    ws += kAwqBatch * align256(meta);
+    double *partials = reinterpret_cast<double *>(ws);  // [kAwqBatch][blocks]
+    // per-point strides in elements (every slot is a multiple of 256 bytes)
+    const int64_t x_stride = align256(a.t * a.k * 2) / 2, s_stride = align256(a.k * 4) / 4;
+    const int64_t code_stride = align256(a.n * a.k / 2), meta_stride = align256(meta) / 4;
+    const int64_t blocks = w4a16_gemm_blocks(a.t, a.n);
 
     hipError_t e;
     if ((e = launch_gemm_bf16(a.x, a.w, a.t, a.n, a.k, y_ref, st)) != hipSuccess) return e;
@@ -317,17 +319,25 @@ hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st) {
     const uint32_t kblocks = (uint32_t)((a.k + 255) / 256);
     const int64_t x8 = a.t * a.k / 8;
     const uint32_t xblocks = (uint32_t)((x8 + 255) / 256 < 4096 ? (x8 + 255) / 256 : 4096);
-    const int64_t ty = a.t * a.n;
-    const QuantArgs q{a.w, a.n, a.k, 4, a.symmetric, a.group, s, a.codes, a.scales, a.zeros};
-    const WoArgs g{xa, a.t, a.codes, a.scales, a.zeros, a.n, a.k, a.symmetric, a.group, y_q};
-    for (int i = 0; i <= a.n_grid; ++i) {
-        hipLaunchKernelGGL(awq_scale_kernel, dim3(kblocks), dim3(256), 0, st, a.sx, (int)a.k, i, a.n_grid, s);
-        hipLaunchKernelGGL(div_act_kernel, dim3(xblocks), dim3(256), 0, st, a.x, x8, (int)a.k, s, xa);
+    for (int i0 = 0; i0 <= a.n_grid; i0 += kAwqBatch) {
+        const int points = a.n_grid + 1 - i0 < kAwqBatch ? a.n_grid + 1 - i0 : kAwqBatch;
+        // the batch's scales and scaled activations, one launch each
+        hipLaunchKernelGGL(awq_scale_kernel, dim3(kblocks, (uint32_t)points), dim3(256), 0, st, a.sx, (int)a.k, i0,
+                           a.n_grid, s, s_stride);
+        hipLaunchKernelGGL(div_act_kernel, dim3(xblocks, (uint32_t)points), dim3(256), 0, st, a.x, x8, (int)a.k, s,
+                           s_stride, xa, x_stride);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_quantize(q, st)) != hipSuccess) return e;
-        if ((e = launch_w4a16_gemm(g, st)) != hipSuccess) return e;
-        hipLaunchKernelGGL(sqerr_partial_kernel, dim3(kSqBlocks), dim3(256), 0, st, y_ref, y_q, ty, partials);
-        hipLaunchKernelGGL(sqerr_finish_kernel, dim3(1), dim3(256), 0, st, partials, a.losses + i);
+        for (int p = 0; p < points; ++p) {
+            const QuantArgs q{a.w, a.n, a.k, 4, a.symmetric, a.group, s + p * s_stride, codes + p * code_stride,
+                              scales + p * meta_stride, zeros + p * meta_stride};
+            if ((e = launch_quantize(q, st)) != hipSuccess) return e;
+        }
+        const WoArgs g{xa, a.t, codes, scales, zeros, a.n, a.k, a.symmetric, a.group, nullptr};
+        if ((e = launch_w4a16_gemm_loss(g, points, x_stride, code_stride, meta_stride, y_ref, partials, st)) !=
+            hipSuccess)
+            return e;
+        hipLaunchKernelGGL(loss_finish_kernel, dim3((uint32_t)points), dim3(256), 0, st, partials, blocks,
+                           a.losses + i0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(awq_pick_kernel, dim3(kblocks), dim3(256), 0, st, a.losses, a.n_grid, a.sx, (int)a.k,

@@ -57,13 +57,29 @@ constexpr int kWaitVm0 = 0x0F70;
 
 LQ_DEVICE int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-template <bool SYM>
+// Several products of the same shape in one launch (the AWQ grid points):
+// blockIdx.y selects one, whose operands sit at the given element strides
+// from the first. LOSS: instead of storing y, the block adds up
+// (yref - y)^2 over its outputs in fp64 (lane order, then the waves in a
+// fixed order) and writes the sum to loss[blockIdx.y * gridDim.x + blockIdx.x].
+struct GemmBatch {
+    int64_t x_stride, code_stride, meta_stride;
+    const float *yref;
+    double *loss;
+};
+
+template <bool SYM, bool LOSS>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
                                                        const uint8_t *__restrict__ codes,
                                                        const float *__restrict__ scales,
                                                        const float *__restrict__ zeros, int group,
-                                                       float *__restrict__ y) {
+                                                       float *__restrict__ y, GemmBatch batch) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
+    __shared__ double wave_loss[4];
+    x += (int64_t)blockIdx.y * batch.x_stride;
+    codes += (int64_t)blockIdx.y * batch.code_stride;
+    scales += (int64_t)blockIdx.y * batch.meta_stride;
+    if (!SYM) zeros += (int64_t)blockIdx.y * batch.meta_stride;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,28 +236,68 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     // exits; the builtin also tells the compiler nothing is pending
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // epilogue: lane holds Y[row 4 kq + v][col l16] of each 16 x 16 tile
+    if constexpr (LOSS) {
+        double sq = 0.0;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
-                const int col = n0 + wn * 64 + nt * 16 + l16;
-                if (row < m && col < n) y[(int64_t)row * n + col] = acc[mt][nt][v];
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
+                    const int col = n0 + wn * 64 + nt * 16 + l16;
+                    if (row < m && col < n) {
+                        const double d = (double)batch.yref[(int64_t)row * n + col] - (double)acc[mt][nt][v];
+                        sq = __builtin_fma(d, d, sq);
+                    }
+                }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+        if (lane == 0) wave_loss[wave] = sq;
+        __syncthreads();
+        if (tid == 0)
+            batch.loss[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
+                ((wave_loss[0] + wave_loss[1]) + wave_loss[2]) + wave_loss[3];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
+                    const int col = n0 + wn * 64 + nt * 16 + l16;
+                    if (row < m && col < n) y[(int64_t)row * n + col] = acc[mt][nt][v];
+                }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st) {
     const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
+    const GemmBatch one{0, 0, 0, nullptr, nullptr};
     if (a.symmetric)
-        hipLaunchKernelGGL(gemm_w4_kernel<true>, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k,
-                           a.codes, a.scales, a.zeros, (int)a.group, a.y);
+        hipLaunchKernelGGL((gemm_w4_kernel<true, false>), dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
+                           (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, one);
     else
-        hipLaunchKernelGGL(gemm_w4_kernel<false>, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
-                           (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y);
+        hipLaunchKernelGGL((gemm_w4_kernel<false, false>), dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
+                           (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, one);
+    return hipGetLastError();
+}
+
+int64_t w4a16_gemm_blocks(int64_t m, int64_t n) { return ((n + BN - 1) / BN) * ((m + BM - 1) / BM); }
+
+hipError_t launch_w4a16_gemm_loss(const WoArgs &a, int points, int64_t x_stride, int64_t code_stride,
+                                  int64_t meta_stride, const float *yref, double *loss, hipStream_t st) {
+    const uint32_t blocks = (uint32_t)w4a16_gemm_blocks(a.m, a.n);
+    const GemmBatch b{x_stride, code_stride, meta_stride, yref, loss};
+    if (a.symmetric)
+        hipLaunchKernelGGL((gemm_w4_kernel<true, true>), dim3(blocks, (uint32_t)points), dim3(256), 0, st, a.x,
+                           (int)a.m, (int)a.n, (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, b);
+    else
+        hipLaunchKernelGGL((gemm_w4_kernel<false, true>), dim3(blocks, (uint32_t)points), dim3(256), 0, st, a.x,
+                           (int)a.m, (int)a.n, (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, b);
     return hipGetLastError();
 }
 

@@ -126,6 +126,13 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
 hipError_t launch_w4a16_gemv(const WoArgs &a, hipStream_t st);
 hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st);
+// `points` products of a's shape in one launch, point p's activations,
+// codes and scales / zeros at p times the given element strides from a's;
+// each workgroup writes sum (yref - y)^2 over its outputs (fp64) to
+// loss[p * blocks + block], blocks = w4a16_gemm_blocks(m, n); y is not stored.
+int64_t w4a16_gemm_blocks(int64_t m, int64_t n);
+hipError_t launch_w4a16_gemm_loss(const WoArgs &a, int points, int64_t x_stride, int64_t code_stride,
+                                  int64_t meta_stride, const float *yref, double *loss, hipStream_t st);
 hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st);
 hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st);
 hipError_t launch_quant_per_token(const TokenQuantArgs &a, hipStream_t st);
