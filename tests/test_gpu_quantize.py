@@ -49,6 +49,20 @@ def test_large_groups_and_per_channel(bits, sym, group):
     _run(w, bits, sym, g)
 
 
+# Groups above 128 run one workgroup per group in strides of 2048 elements:
+# a group of 384 (one partial stride), 2176 (a full and a partial one), and
+# 3 to 4 or more full strides; per-channel groups with a column scale.
+@pytest.mark.parametrize("group,k", [(384, 1536), (2048 + 128, 4352), (6144, 6144), (8192, 8192),
+                                     (8192 + 128, 8320)])
+@pytest.mark.parametrize("bits,sym", [(8, True), (4, False)])
+def test_large_group_strides(group, k, bits, sym):
+    rng = np.random.default_rng(group + bits)
+    n = 19
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * np.logspace(-2, 1, n)[:, None])
+    cs = np.exp(rng.uniform(-2, 2, k)).astype(np.float32) if group == k else None
+    _run(w, bits, sym, group, cs)
+
+
 @pytest.mark.parametrize("bits,sym,group", [(8, True, "k"), (4, False, 128), (8, True, 128)])
 def test_col_scale(bits, sym, group):
     rng = np.random.default_rng(4)
