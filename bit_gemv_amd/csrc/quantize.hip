@@ -236,26 +236,71 @@ __global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restr
     }
 }
 
-// Larger groups (any multiple of 128, including group == k): one 256-lane
-// block per group, two passes over the group (statistics, then codes; the
-// second pass hits L2).
-template <int BITS, bool SYM, bool CS>
-__global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restrict__ w, int64_t group,
+// Larger groups (any multiple of 128, including group == k): one block of
+// TPB lanes per group, read in chunks of kBigLoads * TPB * 8 elements (each
+// lane's kBigLoads 16-byte loads issued before any arithmetic). Statistics
+// run over every chunk, then codes are formed from the chunk still in
+// registers and from re-reads of the others, so a group of up to one chunk
+// is read from memory once: 8192 elements with 256 lanes, 32768 with 1024.
+// Measured on MI355X, INT8 per channel with column scales, weights cold in
+// HBM: 8192 x 8192 in 42 us, 28672 x 8192 in 143 us, where one dependent
+// load at a time per lane took 63 and 202 us.
+constexpr int kBigLoads = 4;
+
+// Elements c0 + 8 t + 8 TPB i .. + 7 (i < kBigLoads) of the group at `base`,
+// times their column scales; lanes past the group read nothing.
+template <int TPB, bool CS, bool NT>
+LQ_DEVICE void load_chunk(const uint16_t *__restrict__ w, const float *__restrict__ cs, int64_t base,
+                          int64_t group, int64_t k, int64_t c0, int t, float x[kBigLoads][8]) {
+    u32x4 v[kBigLoads];
+    f32x4 c[kBigLoads][2];
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+        const int64_t e = c0 + t * 8 + 8 * TPB * i;
+        const bool in = e < group;
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(w + base + e);
+        v[i] = !in ? u32x4{0u, 0u, 0u, 0u} : NT ? __builtin_nontemporal_load(p) : *p;
+        if (CS) {
+            const int64_t col = in ? (base + e) % k : 0;
+            c[i][0] = *reinterpret_cast<const f32x4 *>(cs + col);
+            c[i][1] = *reinterpret_cast<const f32x4 *>(cs + col + 4);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+        unpack8(v[i], x[i]);
+        if (CS) {
+            x[i][0] *= c[i][0].x; x[i][1] *= c[i][0].y; x[i][2] *= c[i][0].z; x[i][3] *= c[i][0].w;
+            x[i][4] *= c[i][1].x; x[i][5] *= c[i][1].y; x[i][6] *= c[i][1].z; x[i][7] *= c[i][1].w;
+        }
+    }
+}
+
+// ONE: the group fits one chunk (read once, streaming).
+template <int BITS, bool SYM, bool CS, bool ONE, int TPB>
+__global__ __launch_bounds__(TPB) void quant_big_kernel(const uint16_t *__restrict__ w, int64_t group,
                                                          int64_t k, const float *__restrict__ cs,
                                                          uint8_t *__restrict__ codes,
                                                          float *__restrict__ scales,
                                                          float *__restrict__ zeros) {
-    __shared__ float red[3][4];
+    constexpr int kWaves = TPB / 64;
+    constexpr int64_t kChunk = (int64_t)kBigLoads * TPB * 8;
+    __shared__ float red[3][kWaves];
     const int64_t g = blockIdx.x;
     const int64_t base = g * group;
     const int t = threadIdx.x;
+    const int64_t nch = ONE ? 1 : (group + kChunk - 1) / kChunk;
     GroupStats<SYM> st;
     st.init();
-    for (int64_t e = t * 8; e < group; e += 2048) {
-        float x[8];
-        load8<CS, false>(w, cs, base + e, CS ? (base + e) % k : 0, x);
+    float x[kBigLoads][8];
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        load_chunk<TPB, CS, ONE>(w, cs, base, group, k, ch * kChunk, t, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st.add(x[i]);
+        for (int i = 0; i < kBigLoads; ++i)
+            if (ch * kChunk + t * 8 + 8 * TPB * i < group) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) st.add(x[i][j]);
+            }
     }
     float a = 0.f, mn = 0.f, mx = 0.f;
     if (SYM) {
@@ -271,11 +316,14 @@ __global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restri
         red[2][wave] = mx;
     }
     __syncthreads();
-    if (SYM) {
-        a = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    } else {
-        mn = fminf(fminf(red[1][0], red[1][1]), fminf(red[1][2], red[1][3]));
-        mx = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    a = red[0][0];
+    mn = red[1][0];
+    mx = red[2][0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) {
+        a = fmaxf(a, red[0][i]);
+        mn = fminf(mn, red[1][i]);
+        mx = fmaxf(mx, red[2][i]);
     }
     float s, z, y = 0.0f;
     const bool fast = fast_group(SYM ? a : fmaxf(-mn, mx));  // block-uniform
@@ -283,24 +331,23 @@ __global__ __launch_bounds__(256) void quant_big_kernel(const uint16_t *__restri
         scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
     else
         scale_zero<BITS, SYM>(a, mn, mx, s, z);
-    for (int64_t e = t * 8; e < group; e += 2048) {
-        float x[8];
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(w + base + e);
-        unpack8(v, x);
-        if (CS) {
-            const int64_t col = (base + e) % k;
+    // the last chunk is still in x; the others are read again
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        if (ch != nch - 1) load_chunk<TPB, CS, false>(w, cs, base, group, k, ch * kChunk, t, x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = x[i] * cs[col + i];
+        for (int i = 0; i < kBigLoads; ++i) {
+            const int64_t e = ch * kChunk + t * 8 + 8 * TPB * i;
+            if (e >= group) continue;
+            int q[8];
+            if (fast) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][j] / s, z);
+            }
+            store8<BITS, SYM>(codes, base + e, q);
         }
-        int q[8];
-        if (fast) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = code_fast<BITS, SYM>(div_rn(x[i], s, y), z);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = code_of_quotient<BITS, SYM>(x[i] / s, z);
-        }
-        store8<BITS, SYM>(codes, base + e, q);
     }
     if (t == 0) {
         scales[g] = s;
@@ -356,9 +403,15 @@ static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
         const int64_t blocks = (ngroups + 16 * kGroupsPerTeam - 1) / (16 * kGroupsPerTeam);
         hipLaunchKernelGGL((quant_g128_kernel<BITS, SYM, CS, kGroupsPerTeam>), dim3((uint32_t)blocks), dim3(256), 0, st,
                            a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
-    } else {
-        hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS>), dim3((uint32_t)ngroups), dim3(256), 0, st,
+    } else if (a.group <= kBigLoads * 256 * 8) {
+        hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS, true, 256>), dim3((uint32_t)ngroups), dim3(256), 0, st,
                            a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    } else if (a.group <= kBigLoads * 1024 * 8) {
+        hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS, true, 1024>), dim3((uint32_t)ngroups), dim3(1024), 0,
+                           st, a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    } else {
+        hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS, false, 1024>), dim3((uint32_t)ngroups), dim3(1024), 0,
+                           st, a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);
     }
     return hipGetLastError();
 }

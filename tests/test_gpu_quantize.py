@@ -49,11 +49,17 @@ def test_large_groups_and_per_channel(bits, sym, group):
     _run(w, bits, sym, g)
 
 
-# Groups above 128 run one workgroup per group in strides of 2048 elements:
-# a group of 384 (one partial stride), 2176 (a full and a partial one), and
-# 3 to 4 or more full strides; per-channel groups with a column scale.
+# Groups above 128 run one workgroup per group, four strides per lane held in
+# registers at a time: 256 lanes (2048-element strides) up to 8192 elements,
+# 1024 lanes (8192-element strides) above. A group of 384 (one partial
+# stride), 2176 (a full and a partial one), 3 or 4 full strides, 8320 (the
+# first 1024-lane size), groups of 2 to 4 strides of 8192 (two groups per
+# row, a partial last stride), then groups over two and three 32768-element
+# chunks (re-read before their codes); per-channel groups with a column scale.
 @pytest.mark.parametrize("group,k", [(384, 1536), (2048 + 128, 4352), (6144, 6144), (8192, 8192),
-                                     (8192 + 128, 8320)])
+                                     (8192 + 128, 8320), (3 * 8192 + 2048 + 128, 3 * 8192 + 2048 + 128),
+                                     (16384, 32768), (28672, 28672), (32768 + 384, 32768 + 384),
+                                     (2 * 32768 + 8192 + 128, 2 * 32768 + 8192 + 128)])
 @pytest.mark.parametrize("bits,sym", [(8, True), (4, False)])
 def test_large_group_strides(group, k, bits, sym):
     rng = np.random.default_rng(group + bits)

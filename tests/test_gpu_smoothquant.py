@@ -28,6 +28,22 @@ def test_smooth_scale_alpha_half(t, n, k):
     assert_same_bits(s, oracle.smooth_scale(x, w, 0.5), "s")
 
 
+def test_smooth_scale_rows_past_grid_extent():
+    """More 64-row tiles of W than a grid's y extent (65535) holds: blocks
+    stride over the rest. Large values planted in the last tile's rows must
+    reach s."""
+    n, k = 65535 * 64 + 70, 128
+    x, w0 = _xw(4, 256, k, seed=5)
+    w = np.tile(w0, (n // 256 + 1, 1))[:n].copy()
+    big = f32_to_bf16_bits(np.array([3.0, -5.0, 7.0]))
+    w[n - 1, 3], w[65535 * 64 + 5, 50], w[65535 * 64, 127] = big
+    say(f"smooth_scale t=4 n={n} k={k}")
+    s = host(bg.smooth_scale(dev_bf16(x), dev_bf16(w), 0.5))
+    ref = oracle.smooth_scale(x, w, 0.5)
+    assert ref[3] != oracle.smooth_scale(x, w[:65535 * 64], 0.5)[3]
+    assert_same_bits(s, ref, "s")
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.25, 0.8, 1.0])
 def test_smooth_scale_other_alpha(alpha):
     x, w = _xw(33, 70, 1024, seed=2)
