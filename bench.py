@@ -84,6 +84,32 @@ def _graph_ms(fn, reps: int) -> float:
     return (time.perf_counter() - t0) * 1e3 / reps
 
 
+def _graph_per_call_ms(fn, calls: int, reps: int = 3) -> float:
+    """Average ms of one fn() call: `calls` calls captured in one HIP graph,
+    its replays bracketed by HIP events. For short kernels, whose eager
+    launches would time the host's submission rate rather than the GPU."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * calls)
+
+
 def _timed(fn, reps: int = 5) -> float:
     """Average ms of fn() over reps launches, bracketed by HIP events on the
     current stream after one untimed call."""
@@ -306,7 +332,7 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
     n, k = shapes[j]
     out = torch.empty((n, k), dtype=torch.float32, device=dev)
     it = iter(range(10 ** 9))
-    ms = _timed(lambda: bg.dequantize_groupwise(packed[next(it) % len(packed)][j], out), reps=10)
+    ms = _graph_per_call_ms(lambda: bg.dequantize_groupwise(packed[next(it) % len(packed)][j], out), calls=20)
     pw = packed[0][j]
     byt = pw.nbytes() + n * k * 4
     rows["dequantize"] = {"shape": [n, k], "ms": round(ms, 4), "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
@@ -347,19 +373,24 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
     ws = [w] + [w.clone() for _ in range(int(2e9 // (nn * kk * 2)))]
     it = iter(range(10 ** 9))
     s = bg.smooth_scale(x, w, alpha)
-    ms = _timed(lambda: bg.smooth_scale(x, ws[next(it) % len(ws)], alpha, s=s), reps=10)
+    ms = _graph_per_call_ms(lambda: bg.smooth_scale(x, ws[next(it) % len(ws)], alpha, s=s), calls=len(ws))
     r["smooth_scale"] = {"ms": round(ms, 4), "GBps": round((t * kk * 2 + nn * kk * 2) / (ms * 1e-3) / 1e9, 1)}
     pwq = bg.quantize_groupwise(w, 8, True, kk, s)
-    ms = _timed(lambda: bg.quantize_groupwise(ws[next(it) % len(ws)], 8, True, kk, s, out=pwq), reps=10)
+    ms = _graph_per_call_ms(lambda: bg.quantize_groupwise(ws[next(it) % len(ws)], 8, True, kk, s, out=pwq),
+                            calls=len(ws))
     r["quantize_w_int8_per_channel"] = {"ms": round(ms, 4),
                                         "GBps": round((nn * kk * 3 + nn * 4) / (ms * 1e-3) / 1e9, 1)}
     del ws
     qx, sx = bg.quant_per_token_int8(x, s)
-    ms = _timed(lambda: bg.quant_per_token_int8(x, s, qx, sx))
+    # 64 copies of X (512 MB in all) in turn, read from HBM as W above
+    xs = [x] + [x.clone() for _ in range(63)]
+    ms = _graph_per_call_ms(lambda: bg.quant_per_token_int8(xs[next(it) % len(xs)], s, qx, sx), calls=len(xs))
+    del xs
     r["quant_per_token_int8"] = {"ms": round(ms, 4), "GBps": round((t * kk * 3 + t * 4) / (ms * 1e-3) / 1e9, 1)}
     try:
         y, acc = bg.w8a8_gemm(qx, sx, pwq.codes.view(torch.int8), pwq.scales.view(-1), want_acc=True)
-        ms = _timed(lambda: bg.w8a8_gemm(qx, sx, pwq.codes.view(torch.int8), pwq.scales.view(-1), y=y, acc=acc))
+        ms = _graph_per_call_ms(
+            lambda: bg.w8a8_gemm(qx, sx, pwq.codes.view(torch.int8), pwq.scales.view(-1), y=y, acc=acc), calls=10)
         tops = 2.0 * t * nn * kk / (ms * 1e-3) / 1e12
         r["w8a8_gemm"] = {"ms": round(ms, 4), "TOPs": round(tops, 1), "bound": "mfma",
                           "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
