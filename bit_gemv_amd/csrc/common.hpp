@@ -55,20 +55,6 @@ LQ_DEVICE float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Max / min over each aligned row of 16 lanes, result in every lane: the
-// partners l ^ 15, l ^ 7, l ^ 2, l ^ 1 together reach all 16 lanes.
-LQ_DEVICE float row16_max(float v) {
-    v = fmaxf(v, dpp_move<kDppMirror>(v));
-    v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_move<kDppXor2>(v));
-    return fmaxf(v, dpp_move<kDppXor1>(v));
-}
-LQ_DEVICE float row16_min(float v) {
-    v = fminf(v, dpp_move<kDppMirror>(v));
-    v = fminf(v, dpp_move<kDppHalfMirror>(v));
-    v = fminf(v, dpp_move<kDppXor2>(v));
-    return fminf(v, dpp_move<kDppXor1>(v));
-}
 
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3).
 // Loads whose offset falls outside return zeros instead of faulting.

@@ -204,66 +204,98 @@ LQ_DEVICE void store8_fast(uint8_t *__restrict__ codes, int64_t elem, const floa
     }
 }
 
-constexpr int kGroupsPerTeam = 4;  // measured on MI355X
+// Max / min over each aligned team of TS (16 or 8) lanes, result in every
+// lane: the DPP partners l ^ 15 (16-lane teams only), l ^ 7, l ^ 2, l ^ 1
+// together reach every lane of the team.
+template <int TS>
+LQ_DEVICE float team_dpp_max(float v) {
+    static_assert(TS == 16 || TS == 8, "teams of 16 or 8 lanes");
+    if (TS == 16) v = fmaxf(v, dpp_move<kDppMirror>(v));
+    v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_move<kDppXor2>(v));
+    return fmaxf(v, dpp_move<kDppXor1>(v));
+}
+template <int TS>
+LQ_DEVICE float team_dpp_min(float v) {
+    static_assert(TS == 16 || TS == 8, "teams of 16 or 8 lanes");
+    if (TS == 16) v = fminf(v, dpp_move<kDppMirror>(v));
+    v = fminf(v, dpp_move<kDppHalfMirror>(v));
+    v = fminf(v, dpp_move<kDppXor2>(v));
+    return fminf(v, dpp_move<kDppXor1>(v));
+}
 
-// group == 128: a team of 16 lanes owns a group, 8 elements (16 bytes of
-// bf16) per lane, and each team takes GPT groups. A block's 16 GPT groups are
-// contiguous and its load i covers groups 16 i .. 16 i + 15 of them (1 KB per
-// wave, coalesced); all GPT loads are issued before any group is computed.
-// Groups tile the rows contiguously, so group index g covers elements
-// [128 g, 128 g + 128) of the flattened matrix and its scale sits at
-// scales[g].
-template <int BITS, bool SYM, bool CS, int GPT>
-__global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restrict__ w,
+// Groups of G = 8 TS M elements: a team of TS lanes (16 or 8) owns a group,
+// 8 elements (16 bytes of bf16) per lane in each of its M chunks of 8 TS
+// elements, and each team takes GPT groups. A block's (256 / TS) GPT groups
+// are contiguous; load (i, c) covers chunk c of one group per team, 16 TS
+// contiguous bytes (whole 128-byte lines); all GPT M loads are issued before
+// any group is computed. Groups tile the rows contiguously (G divides k), so
+// group index g covers elements [G g, G g + G) of the flattened matrix and
+// its scale sits at scales[g].
+template <int BITS, bool SYM, bool CS, int TS, int M, int GPT>
+__global__ __launch_bounds__(256) void quant_team_kernel(const uint16_t *__restrict__ w,
                                                           int64_t ngroups, int64_t k,
                                                           const float *__restrict__ cs,
                                                           uint8_t *__restrict__ codes,
                                                           float *__restrict__ scales,
                                                           float *__restrict__ zeros) {
-    const int team = threadIdx.x >> 4;
-    const int l = threadIdx.x & 15;
-    const int64_t g0 = (int64_t)blockIdx.x * (16 * GPT) + team;
-    float x[GPT][8];
+    constexpr int kTeams = 256 / TS;
+    constexpr int kChunk = 8 * TS;
+    constexpr int G = kChunk * M;
+    const int team = threadIdx.x / TS;
+    const int l = threadIdx.x % TS;
+    const int64_t g0 = (int64_t)blockIdx.x * (kTeams * GPT) + team;
+    float x[GPT][M][8];
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
-        const int64_t g = g0 + 16 * i;
+        const int64_t g = g0 + kTeams * i;
         if (g < ngroups) {  // team-uniform
-            const int64_t elem = g * 128 + l * 8;
-            load8<CS, true>(w, cs, elem, CS ? elem % k : 0, x[i]);
+#pragma unroll
+            for (int c = 0; c < M; ++c) {
+                const int64_t elem = g * G + kChunk * c + l * 8;
+                load8<CS, true>(w, cs, elem, CS ? elem % k : 0, x[i][c]);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
-        const int64_t g = g0 + 16 * i;
+        const int64_t g = g0 + kTeams * i;
         if (g >= ngroups) break;  // team-uniform; later groups are past the end too
-        const int64_t elem = g * 128 + l * 8;
         GroupStats<SYM> st;
         st.init();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st.add(x[i][j]);
+        for (int c = 0; c < M; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st.add(x[i][c][j]);
         float a = 0.f, mn = 0.f, mx = 0.f;
         if (SYM) {
-            a = row16_max(st.a);
+            a = team_dpp_max<TS>(st.a);
         } else {
-            mn = row16_min(st.mn);
-            mx = row16_max(st.mx);
+            mn = team_dpp_min<TS>(st.mn);
+            mx = team_dpp_max<TS>(st.mx);
         }
         float s, z;
         // the 16-lane team takes one branch: it shares the extremes
         if (fast_group(SYM ? a : fmaxf(-mn, mx))) {
             float y;
             scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
-            float c[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][j], s, y), z);
-            store8_fast<BITS, SYM>(codes, elem, c);
+            for (int c = 0; c < M; ++c) {
+                float cf[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cf[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][c][j], s, y), z);
+                store8_fast<BITS, SYM>(codes, g * G + kChunk * c + l * 8, cf);
+            }
         } else {
             scale_zero<BITS, SYM>(a, mn, mx, s, z);
-            int q[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][j] / s, z);
-            store8<BITS, SYM>(codes, elem, q);
+            for (int c = 0; c < M; ++c) {
+                int q[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[i][c][j] / s, z);
+                store8<BITS, SYM>(codes, g * G + kChunk * c + l * 8, q);
+            }
         }
         if (l == 0) {
             scales[g] = s;
@@ -272,7 +304,7 @@ __global__ __launch_bounds__(256) void quant_g128_kernel(const uint16_t *__restr
     }
 }
 
-// Larger groups (any multiple of 128, including group == k): one block of
+// Groups above 1024 elements (per-channel rows of k > 1024 included): one block of
 // TPB lanes per group, read in chunks of kBigLoads * TPB * 8 elements (each
 // lane's kBigLoads 16-byte loads issued before any arithmetic). Statistics
 // run over every chunk, then codes are formed from the chunk still in
@@ -434,13 +466,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     }
 }
 
+// Team shapes (measured on MI355X, INT4 asymmetric, weights cold in HBM):
+// G = 128 on 8-lane teams with two 64-element chunks per lane and two groups
+// per team; 57344 x 8192 in 209-235 us against 243-305 us on 16-lane teams
+// (the per-group extremes, scale and zero are formed by every lane of a
+// team, so fewer lanes per group do less of that work) and 345 us on 4-lane
+// teams (each load then covers parts of cache lines). G = 256 and 512 stay on
+// 16-lane teams (two or four chunks per lane): 8-lane teams were 20-40 %
+// slower there. G = 256: 203 us on the same matrix.
+template <int BITS, bool SYM, bool CS, int TS, int M, int GPT>
+static hipError_t launch_team(const QuantArgs &a, int64_t ngroups, hipStream_t st) {
+    constexpr int64_t per_block = 256 / TS * GPT;
+    const int64_t blocks = (ngroups + per_block - 1) / per_block;
+    hipLaunchKernelGGL((quant_team_kernel<BITS, SYM, CS, TS, M, GPT>), dim3((uint32_t)blocks), dim3(256), 0, st,
+                       a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    return hipGetLastError();
+}
+
 template <int BITS, bool SYM, bool CS>
 static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
     const int64_t ngroups = a.n * (a.k / a.group);
-    if (a.group == 128) {
-        const int64_t blocks = (ngroups + 16 * kGroupsPerTeam - 1) / (16 * kGroupsPerTeam);
-        hipLaunchKernelGGL((quant_g128_kernel<BITS, SYM, CS, kGroupsPerTeam>), dim3((uint32_t)blocks), dim3(256), 0, st,
-                           a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    if (a.group % 128 == 0 && a.group <= 128 * 8) {
+        switch (a.group / 128) {
+            case 1: return launch_team<BITS, SYM, CS, 8, 2, 2>(a, ngroups, st);
+            case 2: return launch_team<BITS, SYM, CS, 16, 2, 2>(a, ngroups, st);
+            case 3: return launch_team<BITS, SYM, CS, 16, 3, 1>(a, ngroups, st);
+            case 4: return launch_team<BITS, SYM, CS, 16, 4, 1>(a, ngroups, st);
+            case 5: return launch_team<BITS, SYM, CS, 16, 5, 1>(a, ngroups, st);
+            case 6: return launch_team<BITS, SYM, CS, 16, 6, 1>(a, ngroups, st);
+            case 7: return launch_team<BITS, SYM, CS, 16, 7, 1>(a, ngroups, st);
+            default: return launch_team<BITS, SYM, CS, 16, 8, 1>(a, ngroups, st);
+        }
     } else if (a.group <= kBigLoads * 256 * 8) {
         hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS, true, 256>), dim3((uint32_t)ngroups), dim3(256), 0, st,
                            a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);

@@ -49,13 +49,30 @@ def test_large_groups_and_per_channel(bits, sym, group):
     _run(w, bits, sym, g)
 
 
-# Groups above 128 run one workgroup per group, four strides per lane held in
+# Groups of 128 M elements, M = 1..8, run on 16-lane teams with M loads per
+# lane (and 4 / M groups per team for M <= 2); 115 groups leave the last
+# block ragged. Column scales on per-channel rows (group == k).
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("bits,sym", [(4, False), (4, True), (8, True), (8, False)])
+def test_team_groups(m, bits, sym):
+    group = 128 * m
+    rng = np.random.default_rng(100 + 10 * m + bits + sym)
+    n, k = 23, 5 * group
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * np.logspace(-2, 1, n)[:, None])
+    _run(w, bits, sym, group)
+    if bits == 8 and sym:
+        w1 = f32_to_bf16_bits(rng.standard_normal((37, group)))
+        _run(w1, bits, sym, group, np.exp(rng.uniform(-2, 2, group)).astype(np.float32))
+
+
+# Groups above 1024 run one workgroup per group, four strides per lane held in
 # registers at a time: 256 lanes (2048-element strides) up to 8192 elements,
-# 1024 lanes (8192-element strides) above. A group of 384 (one partial
-# stride), 2176 (a full and a partial one), 3 or 4 full strides, 8320 (the
-# first 1024-lane size), groups of 2 to 4 strides of 8192 (two groups per
-# row, a partial last stride), then groups over two and three 32768-element
-# chunks (re-read before their codes); per-channel groups with a column scale.
+# 1024 lanes (8192-element strides) above. A group of 2176 (a full and a
+# partial stride), 3 or 4 full strides, 8320 (the first 1024-lane size),
+# groups of 2 to 4 strides of 8192 (two groups per row, a partial last
+# stride), then groups over two and three 32768-element chunks (re-read
+# before their codes); per-channel groups with a column scale. (384 runs on
+# the 16-lane teams above.)
 @pytest.mark.parametrize("group,k", [(384, 1536), (2048 + 128, 4352), (6144, 6144), (8192, 8192),
                                      (8192 + 128, 8320), (3 * 8192 + 2048 + 128, 3 * 8192 + 2048 + 128),
                                      (16384, 32768), (28672, 28672), (32768 + 384, 32768 + 384),
