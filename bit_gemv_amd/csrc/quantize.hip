@@ -425,6 +425,111 @@ __global__ __launch_bounds__(TPB) void quant_big_kernel(const uint16_t *__restri
     }
 }
 
+// Per-channel rows with column scales (group == k, 1024 < k <= 8192): a
+// block of 256 lanes takes R consecutive rows, which share their columns, so
+// each lane loads the column scales of its elements once for R rows (they
+// cost two 16-byte loads per 16 bytes of weights). The rows are held in
+// registers, as in quant_big_kernel. Measured on MI355X, INT8 of W * s with
+// W cold in HBM (one row per block -> two): 8192 x 8192 42.5 -> 39.6 us,
+// 28672 x 8192 140 -> 126 us (the same rows without column scales: 35 us
+// on 8192 x 8192); k = 4224 and 2048 were 10 % slower with two rows (half
+// the blocks, fewer loads a lane), four rows were slower everywhere, so
+// two rows are taken from k = 6144.
+template <int BITS, bool SYM, int R>
+__global__ __launch_bounds__(256) void quant_rows_cs_kernel(const uint16_t *__restrict__ w, int64_t nrows,
+                                                             int64_t k, const float *__restrict__ cs,
+                                                             uint8_t *__restrict__ codes,
+                                                             float *__restrict__ scales,
+                                                             float *__restrict__ zeros) {
+    __shared__ float red[3][R][4];
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int t = threadIdx.x;
+    float x[R][kBigLoads][8];
+    {
+        u32x4 v[R][kBigLoads];
+        f32x4 c[kBigLoads][2];
+#pragma unroll
+        for (int i = 0; i < kBigLoads; ++i) {
+            const int64_t e = t * 8 + 2048 * i;
+            const bool in = e < k;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[r][i] = in && r0 + r < nrows
+                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w + (r0 + r) * k + e))
+                              : u32x4{0u, 0u, 0u, 0u};
+            c[i][0] = *reinterpret_cast<const f32x4 *>(cs + (in ? e : 0));
+            c[i][1] = *reinterpret_cast<const f32x4 *>(cs + (in ? e : 0) + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < kBigLoads; ++i) {
+                unpack8(v[r][i], x[r][i]);
+                x[r][i][0] *= c[i][0].x; x[r][i][1] *= c[i][0].y; x[r][i][2] *= c[i][0].z; x[r][i][3] *= c[i][0].w;
+                x[r][i][4] *= c[i][1].x; x[r][i][5] *= c[i][1].y; x[r][i][6] *= c[i][1].z; x[r][i][7] *= c[i][1].w;
+            }
+    }
+    const int wave = t >> 6;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        GroupStats<SYM> st;
+        st.init();
+#pragma unroll
+        for (int i = 0; i < kBigLoads; ++i)
+            if (t * 8 + 2048 * i < k) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) st.add(x[r][i][j]);
+            }
+        float a = 0.f, mn = 0.f, mx = 0.f;
+        if (SYM) {
+            a = team_max<64>(st.a);
+        } else {
+            mn = team_min<64>(st.mn);
+            mx = team_max<64>(st.mx);
+        }
+        if ((t & 63) == 0) {
+            red[0][r][wave] = a;
+            red[1][r][wave] = mn;
+            red[2][r][wave] = mx;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = r0 + r;
+        if (row >= nrows) break;  // block-uniform
+        const float a = fmaxf(fmaxf(red[0][r][0], red[0][r][1]), fmaxf(red[0][r][2], red[0][r][3]));
+        const float mn = fminf(fminf(red[1][r][0], red[1][r][1]), fminf(red[1][r][2], red[1][r][3]));
+        const float mx = fmaxf(fmaxf(red[2][r][0], red[2][r][1]), fmaxf(red[2][r][2], red[2][r][3]));
+        float s, z, y = 0.0f;
+        const bool fast = fast_group(SYM ? a : fmaxf(-mn, mx));  // block-uniform
+        if (fast)
+            scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
+        else
+            scale_zero<BITS, SYM>(a, mn, mx, s, z);
+#pragma unroll
+        for (int i = 0; i < kBigLoads; ++i) {
+            const int64_t e = t * 8 + 2048 * i;
+            if (e >= k) continue;
+            if (fast) {
+                float c8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) c8[j] = stored_code_fast<BITS, SYM>(div_rn(x[r][i][j], s, y), z);
+                store8_fast<BITS, SYM>(codes, row * k + e, c8);
+            } else {
+                int q[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = code_of_quotient<BITS, SYM>(x[r][i][j] / s, z);
+                store8<BITS, SYM>(codes, row * k + e, q);
+            }
+        }
+        if (t == 0) {
+            scales[row] = s;
+            if (!SYM) zeros[row] = z;
+        }
+    }
+}
+
 // x_hat = (q - z) * s. A wave takes 512 consecutive elements and lane l the
 // elements 4 l .. 4 l + 3 and 256 + 4 l .. + 3 of them, so each of its two
 // 16-byte stores covers 1 KB of contiguous output (the output is 7 of every
@@ -497,6 +602,13 @@ static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
             case 7: return launch_team<BITS, SYM, CS, 16, 7, 1>(a, ngroups, st);
             default: return launch_team<BITS, SYM, CS, 16, 8, 1>(a, ngroups, st);
         }
+    } else if (CS && a.group == a.k && a.k <= kBigLoads * 256 * 8) {
+        if (a.k >= 6144)
+            hipLaunchKernelGGL((quant_rows_cs_kernel<BITS, SYM, 2>), dim3((uint32_t)((a.n + 1) / 2)), dim3(256), 0, st,
+                               a.w, a.n, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+        else
+            hipLaunchKernelGGL((quant_rows_cs_kernel<BITS, SYM, 1>), dim3((uint32_t)a.n), dim3(256), 0, st, a.w, a.n,
+                               a.k, a.col_scale, a.codes, a.scales, a.zeros);
     } else if (a.group <= kBigLoads * 256 * 8) {
         hipLaunchKernelGGL((quant_big_kernel<BITS, SYM, CS, true, 256>), dim3((uint32_t)ngroups), dim3(256), 0, st,
                            a.w, a.group, a.k, a.col_scale, a.codes, a.scales, a.zeros);

@@ -86,6 +86,19 @@ def test_large_group_strides(group, k, bits, sym):
     _run(w, bits, sym, group, cs)
 
 
+# Per-channel rows with column scales above 1024 channels: one row per block
+# below k = 6144, two rows per block (sharing their column-scale loads) from
+# there; an odd row count leaves the last block with one row.
+@pytest.mark.parametrize("k", [1152, 4096 + 128, 6144, 8192])
+@pytest.mark.parametrize("bits,sym", [(8, True), (8, False), (4, True), (4, False)])
+def test_per_channel_col_scale_rows(k, bits, sym):
+    rng = np.random.default_rng(k + 2 * bits + sym)
+    n = 29
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * np.logspace(-2, 1, n)[:, None])
+    cs = np.exp(rng.uniform(-2, 2, k)).astype(np.float32)
+    _run(w, bits, sym, k, cs)
+
+
 @pytest.mark.parametrize("bits,sym,group", [(8, True, "k"), (4, False, 128), (8, True, 128)])
 def test_col_scale(bits, sym, group):
     rng = np.random.default_rng(4)
