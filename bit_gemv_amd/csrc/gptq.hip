@@ -300,74 +300,83 @@ constexpr int NB = 64;  // panel width of the factorisation
 
 // The diagonal block B = [j0, j0 + 64) of the (updated) H: reverse Cholesky
 // V_BB (H_BB = V_BB V_BB^T, upper) written back into H's block, and its
-// inverse into vinv (64 x 64, zeros below the diagonal). One workgroup; both
-// steps are right-looking with one barrier per step: a step reads the
-// column (row) it finalises unscaled, writes the finished values to a
-// separate array, and updates the part still to be processed:
-//  * Cholesky, column j from the last, on the working block A (= H_BB):
-//    F_ij = A_ij / sqrt(A_jj) (i < j), F_jj = sqrt(A_jj), and
-//    A_il -= A_ij A_lj / A_jj for i, l < j (kept symmetric);
-//  * inverse W = F^-1 from W = I, row m from the last: the final row is
-//    W_m. / F_mm, and W_i. -= (F_im / F_mm) W_m. for i < m.
-__global__ __launch_bounds__(256) void chol_diag_kernel(float *__restrict__ h, int k, int j0,
-                                                        float *__restrict__ vinv) {
-    __shared__ float A[NB][NB + 1];
-    __shared__ float F[NB][NB + 1];
-    __shared__ float W[NB][NB + 1];
-    const int tid = threadIdx.x;
-    const int c = tid & 63, r0 = tid >> 6;  // column of this thread; rows r0, r0 + 4, ...
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int i = e / NB, l = e % NB;
-        // the block's upper triangle is current; mirror it (H is symmetric)
-        A[i][l] = i <= l ? h[(int64_t)(j0 + i) * k + j0 + l] : h[(int64_t)(j0 + l) * k + j0 + i];
-        F[i][l] = 0.0f;
-        W[i][l] = i == l ? 1.0f : 0.0f;
-    }
-    __syncthreads();
+// inverse into vinv (64 x 64, zeros below the diagonal). One wave, no
+// barriers: LDS operations of a wave complete in order, so a column written
+// to LDS is read back by every lane in the same step.
+//  * Cholesky, column j from the last: lane i holds row i of the working
+//    block A in registers. F_ij = A_ij / sqrt(A_jj) (F_jj = sqrt(A_jj), the
+//    same product A_jj rsqrt(A_jj)), then A_il -= F_ij F_lj for l < j, with
+//    column j of F broadcast through LDS; lane i's register j then holds F_ij.
+//  * inverse W = F^-1 from W = I, row m from the last: lane c holds column c
+//    of W; W_mc /= F_mm, then W_ic -= F_im W_mc for i < m, reading column m
+//    of F from a column-major copy of F written to LDS once.
+// Both loops unroll fully, so every register index is a constant. Rows and
+// columns of a lane outside the triangle it owns are updated too: they are
+// never read as results. Measured on MI355X: 54 us per block with four
+// waves and a barrier per step.
+__global__ __launch_bounds__(64) void chol_diag_kernel(float *__restrict__ h, int k, int j0,
+                                                       float *__restrict__ vinv) {
+    __shared__ __attribute__((aligned(16))) float col[NB];
+    __shared__ __attribute__((aligned(16))) float Fc[NB][NB];
+    const int lane = threadIdx.x;
+    // always 1, but opaque to the compiler: each unrolled step below sits in
+    // its own (never skipped) branch, which keeps the straight-line blocks
+    // short enough for the code generator (one 7000-instruction block took
+    // it minutes to compile)
+    int go;
+    asm volatile("s_mov_b32 %0, 1" : "=s"(go));
+    float a[NB];
+    // row `lane` of the symmetric block, from its current upper triangle
+#pragma unroll
+    for (int l = 0; l < NB; ++l)
+        a[l] = lane <= l ? h[(int64_t)(j0 + lane) * k + j0 + l] : h[(int64_t)(j0 + l) * k + j0 + lane];
+#pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
+        if (!go) continue;
         // hardware 1 / sqrt (about 1 ulp; the factor needs fp32 accuracy,
         // not correct rounding); not positive definite: NaN or inf, which
         // propagates to U
-        const float ajj = A[j][j];
-        const float rs = __builtin_amdgcn_rsqf(ajj);
-        if (tid < j) F[tid][j] = A[tid][j] * rs;
-        if (tid == j) F[j][j] = ajj * rs;
-        if (c < j) {
-            // all 32 reads first (the column and this thread's 16 rows), then
-            // the updates: one LDS round trip instead of one per row. Rows
-            // i >= j are updated too, unconditionally: they are finished
-            // and never read again, and the stores need no branches.
-            const float alj = A[c][j] * (rs * rs);
-            float aij[NB / 4], aic[NB / 4];
+        const float ajj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
+        const float f = a[j] * __builtin_amdgcn_rsqf(ajj);
+        a[j] = f;
+        col[lane] = f;
+        // from the top, so that the next pivot column (j - 1) is ready first
 #pragma unroll
-            for (int t = 0; t < NB / 4; ++t) {
-                aij[t] = A[r0 + 4 * t][j];
-                aic[t] = A[r0 + 4 * t][c];
-            }
-#pragma unroll
-            for (int t = 0; t < NB / 4; ++t) A[r0 + 4 * t][c] = __builtin_fmaf(-aij[t], alj, aic[t]);
+        for (int l = (j - 1) & ~3; l >= 0; l -= 4) {
+            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&col[l]);
+            if (l + 3 < j) a[l + 3] = __builtin_fmaf(-f, c4.w, a[l + 3]);
+            if (l + 2 < j) a[l + 2] = __builtin_fmaf(-f, c4.z, a[l + 2]);
+            if (l + 1 < j) a[l + 1] = __builtin_fmaf(-f, c4.y, a[l + 1]);
+            a[l] = __builtin_fmaf(-f, c4.x, a[l]);
         }
-        __syncthreads();
     }
+    // V_BB = F back into H's block (upper triangle: row lane, columns >= lane)
+#pragma unroll
+    for (int l = 0; l < NB; ++l)
+        if (lane <= l) h[(int64_t)(j0 + lane) * k + j0 + l] = a[l];
+    // F column-major in LDS (Fc[l][i] = F_il), written once: the inverse's
+    // steps then only read
+#pragma unroll
+    for (int l = 0; l < NB; ++l) Fc[l][lane] = a[l];
+    float w[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) w[i] = i == lane ? 1.0f : 0.0f;
+#pragma unroll
     for (int m = NB - 1; m >= 0; --m) {
-        const float wmc = W[m][c] * __builtin_amdgcn_rcpf(F[m][m]);
-        if (tid < NB) vinv[m * NB + c] = c >= m ? wmc : 0.0f;
-        // every row is updated: F is zero below the diagonal, and rows
-        // i >= m are finished and not read again
-        float fim[NB / 4], wic[NB / 4];
+        if (!go) continue;
+        const float fmm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[m]), m));
+        w[m] *= __builtin_amdgcn_rcpf(fmm);
 #pragma unroll
-        for (int t = 0; t < NB / 4; ++t) {
-            fim[t] = F[r0 + 4 * t][m];
-            wic[t] = W[r0 + 4 * t][c];
+        for (int i = (m - 1) & ~3; i >= 0; i -= 4) {
+            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&Fc[m][i]);
+            if (i + 3 < m) w[i + 3] = __builtin_fmaf(-c4.w, w[m], w[i + 3]);
+            if (i + 2 < m) w[i + 2] = __builtin_fmaf(-c4.z, w[m], w[i + 2]);
+            if (i + 1 < m) w[i + 1] = __builtin_fmaf(-c4.y, w[m], w[i + 1]);
+            w[i] = __builtin_fmaf(-c4.x, w[m], w[i]);
         }
+    }
 #pragma unroll
-        for (int t = 0; t < NB / 4; ++t) W[r0 + 4 * t][c] = __builtin_fmaf(-fim[t], wmc, wic[t]);
-        __syncthreads();
-    }
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int i = e / NB, l = e % NB;
-        if (i <= l) h[(int64_t)(j0 + i) * k + j0 + l] = F[i][l];
-    }
+    for (int m = 0; m < NB; ++m) vinv[m * NB + lane] = lane >= m ? w[m] : 0.0f;
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float *__restrict__ p, int64_t count) {
@@ -524,7 +533,7 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
     // reverse Cholesky, last panel first
     for (int p = panels - 1; p >= 0; --p) {
         const int64_t j0 = (int64_t)p * NB;
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, h, (int)k, (int)j0, vinv + p * NB * NB);
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, st, h, (int)k, (int)j0, vinv + p * NB * NB);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (j0 == 0) continue;
         // V_AB = H_AB Vinv_BB^T (in place: each workgroup owns 64 rows and
