@@ -39,80 +39,98 @@ namespace lq {
 namespace {
 
 // --------------------------------------------------------------------------
-// fp32 GEMM: C[M][N] = (beta ? C : 0) + sgn * A[M][K] op(B), op(B) = B[K][N]
-// (BT = false) or B^T with B given [N][K] (BT = true). Each output is
-// accumulated in ascending K order with fused multiply-adds onto its start
-// value (sgn is +-1, so sgn * a is exact). 64 x 64 tiles, 256 threads of 4 x 4.
+// The column loop's update C[M][N] -= A[M][128] B[128][N] (A: the block's
+// scaled errors, ld 128; B: the block's rows of U; C: the later columns of
+// W). Each output starts at C and adds its 128 terms in ascending k with
+// fused multiply-adds of -A (exact): the operations of applying each
+// column's update as it is made.
+// 128 x 128 tiles, 256 threads; thread (ty, tx) owns rows 4 ty + [0, 4) and
+// 64 + 4 ty + [0, 4), columns 4 tx + [0, 4) and 64 + 4 tx + [0, 4), so its
+// LDS reads are 16-byte and conflict-free. k in steps of 16 through two LDS
+// buffers; the next step's loads are in registers during the current
+// step's multiply-adds. N is a multiple of 128; rows past M are not stored.
 // --------------------------------------------------------------------------
-template <bool BT>
-// (No __restrict__: the panel step computes V_AB in place over H_AB; each
-// workgroup reads all of its A rows before it writes the same rows of C.)
-__global__ __launch_bounds__(256) void sgemm_kernel(int M, int N, int K, float sgn, const float *A, int64_t lda,
-                                                    const float *B, int64_t ldb, int beta, float *C, int64_t ldc) {
-    __shared__ float As[16][68];
-    __shared__ float Bs[16][68];
+__global__ __launch_bounds__(256) void update128_kernel(int M, int N, const float *__restrict__ A,
+                                                        const float *__restrict__ B, int64_t ldb,
+                                                        float *__restrict__ C, int64_t ldc) {
+    constexpr int T = 128, KS = 16;
+    __shared__ __attribute__((aligned(16))) float As[2][KS][T];
+    __shared__ __attribute__((aligned(16))) float Bs[2][KS][T];
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    float acc[4][4];
+    const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
+    // loads of one k step: A rows i0 + lr (two rows), k 4 lk .. + 3;
+    // B row k0 + kb (two rows), columns j0 + 4 lc .. + 3
+    const int lr = tid >> 2, lk = tid & 3;
+    const int kb = tid >> 5, lc = tid & 31;
+    f32x4 pa[2], pb[2];
+    auto fetch = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
-            acc[r][c] = beta && i < M && j < N ? C[(int64_t)i * ldc + j] : 0.0f;
+        for (int h = 0; h < 2; ++h) {
+            const int i = i0 + lr + 64 * h;
+            pa[h] = i < M ? *reinterpret_cast<const f32x4 *>(A + (int64_t)i * 128 + k0 + 4 * lk)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+            pb[h] = *reinterpret_cast<const f32x4 *>(B + (int64_t)(k0 + kb + 8 * h) * ldb + j0 + 4 * lc);
         }
-    for (int k0 = 0; k0 < K; k0 += 16) {
+    };
+    auto stash = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + 256 * q;
-            {
-                const int row = e >> 4, kk = e & 15;  // A: 64 rows x 16 k
-                const int i = i0 + row, kg = k0 + kk;
-                As[kk][row] = i < M && kg < K ? A[(int64_t)i * lda + kg] : 0.0f;
-            }
-            if (BT) {
-                const int col = e >> 4, kk = e & 15;  // B^T: 64 rows (n) x 16 k
-                const int j = j0 + col, kg = k0 + kk;
-                Bs[kk][col] = j < N && kg < K ? B[(int64_t)j * ldb + kg] : 0.0f;
-            } else {
-                const int kk = e >> 6, col = e & 63;  // B: 16 k x 64 columns
-                const int j = j0 + col, kg = k0 + kk;
-                Bs[kk][col] = j < N && kg < K ? B[(int64_t)kg * ldb + j] : 0.0f;
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int row = lr + 64 * h;
+            As[buf][4 * lk + 0][row] = pa[h].x;
+            As[buf][4 * lk + 1][row] = pa[h].y;
+            As[buf][4 * lk + 2][row] = pa[h].z;
+            As[buf][4 * lk + 3][row] = pa[h].w;
+            *reinterpret_cast<f32x4 *>(&Bs[buf][kb + 8 * h][4 * lc]) = pb[h];
         }
-        __syncthreads();
+    };
+    float acc[8][8];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float a[4], b[4];
+    for (int r = 0; r < 8; ++r) {
+        const int i = i0 + 4 * ty + (r & 3) + 64 * (r >> 2);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = sgn * As[kk][4 * ty + r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = Bs[kk][4 * tx + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 c4 = i < M ? *reinterpret_cast<const f32x4 *>(C + (int64_t)i * ldc + j0 + 4 * tx + 64 * h)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[r][4 * h + 0] = c4.x;
+            acc[r][4 * h + 1] = c4.y;
+            acc[r][4 * h + 2] = c4.z;
+            acc[r][4 * h + 3] = c4.w;
         }
+    }
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int step = 0; step < 128 / KS; ++step) {
+        const int buf = step & 1;
+        if (step + 1 < 128 / KS) fetch((step + 1) * KS);
+        // (unrolled twice: a full unroll hoists every step's LDS reads into
+        // registers and leaves one wave per SIMD)
+#pragma unroll 2
+        for (int kk = 0; kk < KS; ++kk) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&As[buf][kk][4 * ty]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&As[buf][kk][64 + 4 * ty]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&Bs[buf][kk][4 * tx]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&Bs[buf][kk][64 + 4 * tx]);
+            const float a[8] = {-a0.x, -a0.y, -a0.z, -a0.w, -a1.x, -a1.y, -a1.z, -a1.w};
+            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+        }
+        if (step + 1 < 128 / KS) stash(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 8; ++r) {
+        const int i = i0 + 4 * ty + (r & 3) + 64 * (r >> 2);
+        if (i >= M) continue;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int i = i0 + 4 * ty + r, j = j0 + 4 * tx + c;
-            if (i < M && j < N) C[(int64_t)i * ldc + j] = acc[r][c];
-        }
-}
-
-template <bool BT>
-hipError_t sgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B, int64_t ldb,
-                 int beta, float *C, int64_t ldc, hipStream_t st) {
-    if (M <= 0 || N <= 0) return hipSuccess;
-    const dim3 grid((uint32_t)((N + 63) / 64), (uint32_t)((M + 63) / 64));
-    hipLaunchKernelGGL((sgemm_kernel<BT>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn, A, lda, B, ldb, beta,
-                       C, ldc);
-    return hipGetLastError();
+        for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<f32x4 *>(C + (int64_t)i * ldc + j0 + 4 * tx + 64 * h) =
+                f32x4{acc[r][4 * h], acc[r][4 * h + 1], acc[r][4 * h + 2], acc[r][4 * h + 3]};
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -583,9 +601,10 @@ hipError_t launch_gptq_quantize(const GptqArgs &a, hipStream_t st) {
         const int64_t f0 = j0 + GB;
         if (f0 < a.k) {
             // W[:, f0:] = W[:, f0:] - D U[j0:j0+128, f0:], in column order per element
-            if ((e = sgemm<false>(a.n, a.k - f0, GB, -1.0f, dbuf, GB, a.u + j0 * a.k + f0, a.k, 1, wf + f0, a.k, st)) !=
-                hipSuccess)
-                return e;
+            const dim3 grid((uint32_t)((a.k - f0) / 128), (uint32_t)((a.n + 127) / 128));
+            hipLaunchKernelGGL(update128_kernel, grid, dim3(256), 0, st, (int)a.n, (int)(a.k - f0), dbuf,
+                               a.u + j0 * a.k + f0, a.k, wf + f0, a.k);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
     return hipSuccess;
