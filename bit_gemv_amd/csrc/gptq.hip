@@ -18,9 +18,10 @@
 //
 // Two entry points:
 //  * the factor: X^T (bf16, zero-padded to 64 tokens) -> H = X^T X on bf16
-//    MFMA -> 2 H + damping -> blocked reverse Cholesky in 64-wide panels
-//    (the panel's diagonal block factored and inverted by one workgroup in
-//    LDS, panel and trailing updates by an fp32 GEMM) -> blocked inverse of
+//    MFMA -> 2 H + damping -> left-looking blocked reverse Cholesky in
+//    64-wide panels (a panel's columns take the finished panels' terms in
+//    one deep fp32 GEMM, its diagonal block is factored and inverted by one
+//    wave, the panel above is solved by an fp32 GEMM) -> blocked inverse of
 //    V -> U, all fp32;
 //  * the column loop: per 128-column block, one wave per row walks the
 //    block's columns with the block of U in LDS (the codes, the group's
@@ -135,13 +136,11 @@ __global__ __launch_bounds__(256) void update128_kernel(int M, int N, const floa
 
 // --------------------------------------------------------------------------
 // fp32 GEMM on the matrix cores (v_mfma_f32_16x16x4f32) for the factor, where
-// only fp32 accuracy matters (the column loop keeps the GEMM above, whose
-// fixed accumulation order its codes depend on):
+// only fp32 accuracy matters (the column loop keeps the VALU update above,
+// whose fixed accumulation order its codes depend on):
 //   C[M][N] = (beta ? C : 0) + sgn * A[M][K] op(B),
 // op(B) = B[K][N] (BT = false) or B^T with B given [N][K] (BT = true). M, N
-// and K are multiples of 64 (the factor's panels). UPPER: only the 64 x 64
-// output tiles on or above the block diagonal are computed (the trailing
-// update keeps the upper triangle of H, the only part read later). AUPPER:
+// and K are multiples of 64 (the factor's panels). AUPPER:
 // A is upper triangular, so row block i0 starts its sum at k = i0. PARTIAL:
 // blockIdx.z takes the k range [z ksplit, (z + 1) ksplit) and writes its
 // partial sum to C + z M N (ld N, no beta); sum_splits_kernel adds the
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(256) void update128_kernel(int M, int N, const floa
 // B[l / 16][l % 16] of a 16 x 16 x 4 step, and D rows 4 (l / 16) + v of
 // column l % 16.
 // --------------------------------------------------------------------------
-template <bool BT, bool UPPER, bool AUPPER, bool PARTIAL>
+template <bool BT, bool AUPPER, bool PARTIAL>
 __global__ __launch_bounds__(256) void mgemm_kernel(int M, int N, int K, float sgn, const float *A, int64_t lda,
                                                     const float *B, int64_t ldb, int beta, float *C, int64_t ldc,
                                                     int ksplit) {
@@ -162,7 +161,6 @@ __global__ __launch_bounds__(256) void mgemm_kernel(int M, int N, int K, float s
     __shared__ __attribute__((aligned(16))) float As[64 * 20];
     __shared__ __attribute__((aligned(16))) float Bs[BT ? 64 * 20 : 16 * 80];
     const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    if (UPPER && i0 > j0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l16 = lane & 15, lq = lane >> 4;
@@ -229,24 +227,24 @@ __global__ __launch_bounds__(256) void mgemm_kernel(int M, int N, int K, float s
                 C[(int64_t)(i0 + wm * 32 + mt * 16 + 4 * lq + v) * ldc + j0 + wn * 32 + nt * 16 + l16] = acc[mt][nt][v];
 }
 
-template <bool BT, bool UPPER, bool AUPPER>
+template <bool BT, bool AUPPER>
 hipError_t mgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B, int64_t ldb,
                  int beta, float *C, int64_t ldc, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (M % 64 || N % 64 || K % 64) return hipErrorInvalidValue;
     const dim3 grid((uint32_t)(N / 64), (uint32_t)(M / 64));
-    hipLaunchKernelGGL((mgemm_kernel<BT, UPPER, AUPPER, false>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn,
+    hipLaunchKernelGGL((mgemm_kernel<BT, AUPPER, false>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn,
                        A, lda, B, ldb, beta, C, ldc, 0);
     return hipGetLastError();
 }
 
-// C[i][j] = sum over z of part[z][i][j], z in order
+// C[i][j] = (beta ? C[i][j] : 0) + sum over z of part[z][i][j], z in order
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits, int M, int N,
-                                                         float *__restrict__ C, int64_t ldc) {
+                                                         int beta, float *__restrict__ C, int64_t ldc) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)M * N) return;
     const int i = (int)(e / N), j = (int)(e % N);
-    float v = 0.0f;
+    float v = beta ? C[(int64_t)i * ldc + j] : 0.0f;
     for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + e];
     C[(int64_t)i * ldc + j] = v;
 }
@@ -254,21 +252,25 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict
 constexpr int kMaxSplits = 16;  // k ranges of the narrow, deep products
 
 // A narrow product (N = 64) with a deep k: k split into up to kMaxSplits
-// ranges of at least 1024 so that enough workgroups run; the partials go to
-// part (kMaxSplits M N floats) and are summed in order.
+// ranges of at least 128, as many as bring the launch to about 2048
+// workgroups (measured: ranges of at least 1024 left the factor's first
+// panels a few long-running workgroups); the partials go to part
+// (kMaxSplits M N floats) and are added, in order, to beta ? C : 0.
 template <bool BT, bool AUPPER>
 hipError_t mgemm_deep(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int64_t lda, const float *B,
-                      int64_t ldb, float *C, int64_t ldc, float *part, hipStream_t st) {
+                      int64_t ldb, int beta, float *C, int64_t ldc, float *part, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (M % 64 || N % 64 || K % 64) return hipErrorInvalidValue;
-    const int splits = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, K / 1024));
-    if (splits == 1) return mgemm<BT, false, AUPPER>(M, N, K, sgn, A, lda, B, ldb, 0, C, ldc, st);
+    const int64_t tiles = (M / 64) * (N / 64);
+    const int splits = (int)std::min<int64_t>(
+        std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, K / 128)), std::max<int64_t>(1, 2048 / tiles));
+    if (splits == 1) return mgemm<BT, AUPPER>(M, N, K, sgn, A, lda, B, ldb, beta, C, ldc, st);
     const int64_t ksplit = (K / 64 + splits - 1) / splits * 64;
     const dim3 grid((uint32_t)(N / 64), (uint32_t)(M / 64), (uint32_t)splits);
-    hipLaunchKernelGGL((mgemm_kernel<BT, false, AUPPER, true>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn, A,
+    hipLaunchKernelGGL((mgemm_kernel<BT, AUPPER, true>), grid, dim3(256), 0, st, (int)M, (int)N, (int)K, sgn, A,
                        lda, B, ldb, 0, part, N, (int)ksplit);
     hipLaunchKernelGGL(sum_splits_kernel, dim3((uint32_t)((M * N + 255) / 256)), dim3(256), 0, st, part, splits, (int)M,
-                       (int)N, C, ldc);
+                       (int)N, beta, C, ldc);
     return hipGetLastError();
 }
 
@@ -548,19 +550,28 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
     hipLaunchKernelGGL(damp_apply_kernel, dim3(2048), dim3(256), 0, st, h, (int)k, percdamp, dsum);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int panels = (int)(k / NB);
-    // reverse Cholesky, last panel first
+    // reverse Cholesky, last panel first, left-looking: the panel's columns
+    // take all finished panels' contributions in one deep product,
+    //   H[0 : j0 + 64, B] -= V[0 : j0 + 64, D] V[B, D]^T   (D: columns >= j0 + 64),
+    // then its diagonal block is factored and V_AB = H_AB Vinv_BB^T. (Applying
+    // each panel's rank-64 update to the whole remaining triangle instead
+    // reads and writes that triangle once per panel: twice the memory traffic,
+    // 31 % of the factor's time at k = 11008.) V's columns stay in H's upper
+    // triangle; the lower triangles of diagonal blocks are never read.
     for (int p = panels - 1; p >= 0; --p) {
         const int64_t j0 = (int64_t)p * NB;
+        const int64_t kd = k - j0 - NB;
+        if (kd > 0 && (e = mgemm_deep<true, false>(j0 + NB, NB, kd, -1.0f, h + j0 + NB, k, h + j0 * k + j0 + NB, k, 1,
+                                                    h + j0, k, part, st)) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, st, h, (int)k, (int)j0, vinv + p * NB * NB);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (j0 == 0) continue;
         // V_AB = H_AB Vinv_BB^T (in place: each workgroup owns 64 rows and
-        // reads all of them before it writes), then the upper triangle of
-        // H_AA -= V_AB V_AB^T
-        if ((e = mgemm<true, false, false>(j0, NB, NB, 1.0f, h + j0, k, vinv + p * NB * NB, NB, 0, h + j0, k, st)) !=
+        // reads all of them before it writes)
+        if ((e = mgemm<true, false>(j0, NB, NB, 1.0f, h + j0, k, vinv + p * NB * NB, NB, 0, h + j0, k, st)) !=
             hipSuccess)
             return e;
-        if ((e = mgemm<true, true, false>(j0, j0, NB, -1.0f, h + j0, k, h + j0, k, 1, h, k, st)) != hipSuccess) return e;
     }
     // U = V^-1, first panel first: U_BB = Vinv_BB, U_AB = -U_AA (V_AB U_BB)
     hipLaunchKernelGGL(fill_kernel, dim3(2048), dim3(256), 0, st, u, k * k);
@@ -570,11 +581,12 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
         hipLaunchKernelGGL(put_block_kernel, dim3(1), dim3(256), 0, st, vinv + p * NB * NB, u, (int)k, (int)j0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (j0 == 0) continue;
-        if ((e = mgemm<false, false, false>(j0, NB, NB, 1.0f, h + j0, k, u + j0 * k + j0, k, 0, tmp, NB, st)) !=
+        if ((e = mgemm<false, false>(j0, NB, NB, 1.0f, h + j0, k, u + j0 * k + j0, k, 0, tmp, NB, st)) !=
             hipSuccess)
             return e;
         // U_AA is upper triangular: row block i0 sums from k = i0
-        if ((e = mgemm_deep<false, true>(j0, NB, j0, -1.0f, u, k, tmp, NB, u + j0, k, part, st)) != hipSuccess) return e;
+        if ((e = mgemm_deep<false, true>(j0, NB, j0, -1.0f, u, k, tmp, NB, 0, u + j0, k, part, st)) != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }
