@@ -473,8 +473,12 @@ __global__ __launch_bounds__(1024) void gptq_block_kernel(float *__restrict__ w,
     }
     int qa = 0, qb = 0;
     float da = 0.0f, db = 0.0f;
-    for (int j = 0; j < GB; ++j) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(j < 64 ? a : b), j & 63));
+    // Column j: its code and scaled error d from the current value, then every
+    // lane's columns take fma(-d, U_jf, w_f). U is zero below its diagonal,
+    // so that update leaves the columns before j unchanged, and column j's own
+    // value is not read again once its code and d are taken: no lane needs a
+    // predicate. Columns 0..63 sit in a, 64..127 in b.
+    auto step = [&](int j, float wj, float &q_keep, float &d_keep) {
         float qf;
         if (SYM) {
             const float top = (float)((1 << (BITS - 1)) - 1);
@@ -484,18 +488,18 @@ __global__ __launch_bounds__(1024) void gptq_block_kernel(float *__restrict__ w,
             qf = clampf_def(rintf(wj / s) + z, 0.0f, top);
         }
         const float d = (wj - (qf - z) * s) / Us[j][j];
-        if (lane > j) a = __builtin_fmaf(-d, Us[j][lane], a);
-        if (64 + lane > j) b = __builtin_fmaf(-d, Us[j][64 + lane], b);
+        a = __builtin_fmaf(-d, Us[j][lane], a);
+        b = __builtin_fmaf(-d, Us[j][64 + lane], b);
         if (lane == (j & 63)) {
-            if (j < 64) {
-                qa = (int)qf;
-                da = d;
-            } else {
-                qb = (int)qf;
-                db = d;
-            }
+            q_keep = qf;
+            d_keep = d;
         }
-    }
+    };
+    float qfa = 0.0f, qfb = 0.0f;
+    for (int j = 0; j < 64; ++j) step(j, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), j)), qfa, da);
+    for (int j = 64; j < GB; ++j) step(j, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), j - 64)), qfb, db);
+    qa = (int)qfa;
+    qb = (int)qfb;
     dbuf[(int64_t)r * GB + lane] = da;
     dbuf[(int64_t)r * GB + 64 + lane] = db;
     if (BITS == 4) {
