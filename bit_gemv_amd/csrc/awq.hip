@@ -265,8 +265,11 @@ hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int
 // activations sit side by side in the workspace, and one launch of the
 // W4A16 GEMM computes all their products with the squared error against
 // the reference product fused into its epilogue (at n = 4096 one product
-// alone is only 128 workgroups).
-constexpr int kAwqBatch = 4;
+// alone is only 128 workgroups). Measured on MI355X, 512 tokens, 21 grid
+// points, per linear: batches of 11 took 1.30 / 3.01 / 2.94 ms on
+// 4096 x 4096 / 11008 x 4096 / 4096 x 11008, batches of 4 1.39 / 3.45 /
+// 3.18 ms, one batch of 21 1.31 / 3.20 / 3.13 ms.
+constexpr int kAwqBatch = 11;
 
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
     const int64_t meta = n * (k / 128) * 4;  // scales (or zeros) of one point, group >= 128

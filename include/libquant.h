@@ -309,8 +309,11 @@ lq_status act_absmean(const void *x_bf16, int64_t t, int64_t k, float *sx, void 
 
 /*
  * awq_workspace_bytes -- device workspace awq_search needs for these sizes
- * (two fp32 [t][n] outputs, the bf16 [t][k] scaled activations and small
- * vectors); -1 for sizes awq_search would reject as too large or empty.
+ * (the fp32 [t][n] reference product; for each of the 11 grid points it
+ * evaluates together, the bf16 [t][k] scaled activations, the fp32 [k]
+ * scale vector and the packed INT4 codes, scales and zeros of W diag(s);
+ * fp64 loss partials), each piece 256-byte aligned; -1 for sizes
+ * awq_search would reject as too large or empty.
  */
 int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
 

@@ -159,12 +159,12 @@ def test_act_absmean_rejects(lib):
 def test_awq_workspace_bytes(lib):
     assert lib.awq_workspace_bytes(0, 8, 256) == -1
     assert lib.awq_workspace_bytes(16, 8, -1) == -1
-    # the reference product fp32 [t][n]; per grid point of a batch of four:
+    # the reference product fp32 [t][n]; per grid point of a batch of 11:
     # X / s bf16 [t][k], s fp32 [k], codes [n][k/2], scales and zeros fp32
     # [n][k/128]; one fp64 loss partial per GEMM workgroup and point; each
     # piece 256-byte aligned
     per_point = 8192 + 1024 + 1024 + 2 * 256
-    assert lib.awq_workspace_bytes(16, 8, 256) == 512 + 4 * per_point + 256
+    assert lib.awq_workspace_bytes(16, 8, 256) == 512 + 11 * per_point + 256
 
 
 def _awq(lib, x=A16, t=16, w=B16, n=8, k=256, sym=0, group=128, n_grid=20, sx=P(6 << 20), ws=P(7 << 20),
