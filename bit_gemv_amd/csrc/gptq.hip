@@ -326,7 +326,8 @@ constexpr int NB = 64;  // panel width of the factorisation
 //  * Cholesky, column j from the last: lane i holds row i of the working
 //    block A in registers. F_ij = A_ij / sqrt(A_jj) (F_jj = sqrt(A_jj), the
 //    same product A_jj rsqrt(A_jj)), then A_il -= F_ij F_lj for l < j, with
-//    column j of F broadcast through LDS; lane i's register j then holds F_ij.
+//    column j of F broadcast through LDS (two columns per broadcast); lane
+//    i's register j then holds F_ij.
 //  * inverse W = F^-1 from W = I, row m from the last: lane c holds column c
 //    of W; W_mc /= F_mm, then W_ic -= F_im W_mc for i < m, reading column m
 //    of F from a column-major copy of F written to LDS once.
@@ -337,6 +338,7 @@ constexpr int NB = 64;  // panel width of the factorisation
 __global__ __launch_bounds__(64) void chol_diag_kernel(float *__restrict__ h, int k, int j0,
                                                        float *__restrict__ vinv) {
     __shared__ __attribute__((aligned(16))) float col[NB];
+    __shared__ __attribute__((aligned(16))) float col2[NB];
     __shared__ __attribute__((aligned(16))) float Fc[NB][NB];
     const int lane = threadIdx.x;
     // always 1, but opaque to the compiler: each unrolled step below sits in
@@ -351,23 +353,34 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(float *__restrict__ h, in
     for (int l = 0; l < NB; ++l)
         a[l] = lane <= l ? h[(int64_t)(j0 + lane) * k + j0 + l] : h[(int64_t)(j0 + l) * k + j0 + lane];
 #pragma unroll
-    for (int j = NB - 1; j >= 0; --j) {
+    // columns in pairs (j, j - 1), j odd: column j's term on column j - 1
+    // goes through readlane, then both columns are broadcast through LDS
+    // together (one write-to-read round trip per pair); every element takes
+    // column j's term, then column j - 1's, as one column at a time would
+    for (int jj = NB / 2 - 1; jj >= 0; --jj) {
         if (!go) continue;
+        const int j = 2 * jj + 1;
         // hardware 1 / sqrt (about 1 ulp; the factor needs fp32 accuracy,
         // not correct rounding); not positive definite: NaN or inf, which
         // propagates to U
         const float ajj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
         const float f = a[j] * __builtin_amdgcn_rsqf(ajj);
         a[j] = f;
+        const float fj1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j - 1));  // F_{j-1, j}
+        a[j - 1] = __builtin_fmaf(-f, fj1, a[j - 1]);
+        const float aj1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j - 1]), j - 1));
+        const float g = a[j - 1] * __builtin_amdgcn_rsqf(aj1);
+        a[j - 1] = g;
         col[lane] = f;
-        // from the top, so that the next pivot column (j - 1) is ready first
+        col2[lane] = g;
 #pragma unroll
-        for (int l = (j - 1) & ~3; l >= 0; l -= 4) {
+        for (int l = (j - 2) & ~3; l >= 0; l -= 4) {
             const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&col[l]);
-            if (l + 3 < j) a[l + 3] = __builtin_fmaf(-f, c4.w, a[l + 3]);
-            if (l + 2 < j) a[l + 2] = __builtin_fmaf(-f, c4.z, a[l + 2]);
-            if (l + 1 < j) a[l + 1] = __builtin_fmaf(-f, c4.y, a[l + 1]);
-            a[l] = __builtin_fmaf(-f, c4.x, a[l]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&col2[l]);
+            if (l + 3 < j - 1) a[l + 3] = __builtin_fmaf(-g, d4.w, __builtin_fmaf(-f, c4.w, a[l + 3]));
+            if (l + 2 < j - 1) a[l + 2] = __builtin_fmaf(-g, d4.z, __builtin_fmaf(-f, c4.z, a[l + 2]));
+            if (l + 1 < j - 1) a[l + 1] = __builtin_fmaf(-g, d4.y, __builtin_fmaf(-f, c4.y, a[l + 1]));
+            a[l] = __builtin_fmaf(-g, d4.x, __builtin_fmaf(-f, c4.x, a[l]));
         }
     }
     // V_BB = F back into H's block (upper triangle: row lane, columns >= lane)
