@@ -237,6 +237,20 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // epilogue: lane holds Y[row 4 kq + v][col l16] of each 16 x 16 tile
     if constexpr (LOSS) {
+        // all 64 reference loads first (outputs past m or n read element 0
+        // and are skipped below): loads under per-output branches were each
+        // waited for in turn, about 40 us per workgroup
+        float yr[4][4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
+                    const int col = n0 + wn * 64 + nt * 16 + l16;
+                    yr[mt][nt][v] = batch.yref[row < m && col < n ? (int64_t)row * n + col : 0];
+                }
         double sq = 0.0;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -246,10 +260,8 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
                 for (int v = 0; v < 4; ++v) {
                     const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
                     const int col = n0 + wn * 64 + nt * 16 + l16;
-                    if (row < m && col < n) {
-                        const double d = (double)batch.yref[(int64_t)row * n + col] - (double)acc[mt][nt][v];
-                        sq = __builtin_fma(d, d, sq);
-                    }
+                    const double d = (double)yr[mt][nt][v] - (double)acc[mt][nt][v];
+                    if (row < m && col < n) sq = __builtin_fma(d, d, sq);
                 }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
