@@ -68,9 +68,10 @@ __global__ __launch_bounds__(256) void update128_kernel(int M, int N, const floa
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int i = i0 + lr + 64 * h;
-            pa[h] = i < M ? *reinterpret_cast<const f32x4 *>(A + (int64_t)i * 128 + k0 + 4 * lk)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
+            // rows past M read row M - 1: they only feed outputs that are
+            // not stored, and the loads need no branch
+            const int i = min(i0 + lr + 64 * h, M - 1);
+            pa[h] = *reinterpret_cast<const f32x4 *>(A + (int64_t)i * 128 + k0 + 4 * lk);
             pb[h] = *reinterpret_cast<const f32x4 *>(B + (int64_t)(k0 + kb + 8 * h) * ldb + j0 + 4 * lc);
         }
     };
@@ -88,11 +89,10 @@ __global__ __launch_bounds__(256) void update128_kernel(int M, int N, const floa
     float acc[8][8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        const int i = i0 + 4 * ty + (r & 3) + 64 * (r >> 2);
+        const int i = min(i0 + 4 * ty + (r & 3) + 64 * (r >> 2), M - 1);  // rows past M: not stored
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const f32x4 c4 = i < M ? *reinterpret_cast<const f32x4 *>(C + (int64_t)i * ldc + j0 + 4 * tx + 64 * h)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(C + (int64_t)i * ldc + j0 + 4 * tx + 64 * h);
             acc[r][4 * h + 0] = c4.x;
             acc[r][4 * h + 1] = c4.y;
             acc[r][4 * h + 2] = c4.z;
