@@ -238,18 +238,25 @@ hipError_t mgemm(int64_t M, int64_t N, int64_t K, float sgn, const float *A, int
     return hipGetLastError();
 }
 
-// C[i][j] = (beta ? C[i][j] : 0) + sum over z of part[z][i][j], z in order
+constexpr int kMaxSplits = 16;  // k ranges of the narrow, deep products
+
+// C[i][j] = (beta ? C[i][j] : 0) + sum over z of part[z][i][j], z in order.
+// Every partial is loaded before the first addition (a loop over a runtime
+// count waited for each load in turn).
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits, int M, int N,
                                                          int beta, float *__restrict__ C, int64_t ldc) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)M * N) return;
     const int i = (int)(e / N), j = (int)(e % N);
+    float pv[kMaxSplits];
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z) pv[z] = part[(int64_t)min(z, splits - 1) * M * N + e];  // past splits: unused
     float v = beta ? C[(int64_t)i * ldc + j] : 0.0f;
-    for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + e];
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z)
+        if (z < splits) v += pv[z];
     C[(int64_t)i * ldc + j] = v;
 }
-
-constexpr int kMaxSplits = 16;  // k ranges of the narrow, deep products
 
 // A narrow product (N = 64) with a deep k: k split into up to kMaxSplits
 // ranges of at least 128, as many as bring the launch to about 2048
