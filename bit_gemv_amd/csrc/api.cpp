@@ -65,6 +65,8 @@ bool any_overlap(std::initializer_list<Range> outs, std::initializer_list<Range>
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// largest multiple of 128 with k * 128 * 128 < 2^31 (W8A8 int32 accumulators)
+constexpr int64_t kMaxW8a8K = 130944;
 
 lq_status launched(hipError_t e, const char *what) {
     if (e == hipErrorNotSupported) return fail(LQ_ERR_UNSUPPORTED, "%s: not available in this build", what);
@@ -265,7 +267,11 @@ lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *
     const char *fn = "w8a8_gemm";
     if (m < 0 || n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size or k <= 0", fn);
     if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
-    if (k > 131072) return fail(LQ_ERR_UNSUPPORTED, "%s: k > 131072 could overflow the int32 accumulator", fn);
+    // |acc| <= k * 128 * 128 must stay below 2^31: k <= 131071, so at most
+    // 130944 (the last multiple of 128 below it)
+    if (k > kMaxW8a8K)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: k > %lld could overflow the int32 accumulator", fn,
+                    (long long)kMaxW8a8K);
     if (m > kMaxDim || n > kMaxDim) return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
     if (m == 0 || n == 0) return LQ_OK;
     if (!qx || !aligned(qx, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: qx null or not 16-byte aligned", fn);

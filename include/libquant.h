@@ -212,10 +212,12 @@ lq_status quant_per_token_int8(const void *x_bf16, int64_t t, int64_t k, const f
  * INT32 accumulation; "3.6 Quantization" code block: per-token activation
  * scale times per-output-channel weight scale):
  *   acc[i][r] = sum_j qx[i][j] * qw[r][j]   (exact in int32: |acc| <= k * 128^2
- *                                           < 2^31 for k <= 131072)
+ *                                           < 2^31 for k <= 130944)
  *   y[i][r]   = (acc[i][r] * sx[i]) * sw[r] in fp32.
  * qx [m][k], qw [n][k] int8; sx fp32 [m]; sw fp32 [n]; acc out int32 [m][n]
- * (nullable); y out fp32 [m][n]. k multiple of 128 and <= 131072.
+ * (nullable); y out fp32 [m][n]. k multiple of 128 and <= 130944 (the largest
+ * such k with k * 128^2 < 2^31, so any int8 codes are exact; larger k:
+ * LQ_ERR_UNSUPPORTED).
  */
 lq_status w8a8_gemm(const int8_t *qx, const float *sx, int64_t m, const int8_t *qw,
                     const float *sw, int64_t n, int64_t k, int32_t *acc, float *y, void *stream);

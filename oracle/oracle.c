@@ -685,17 +685,24 @@ int oracle_mx_matmul(const uint16_t *x, int64_t m, const uint8_t *codes, const u
  *    first column is reached; codes round as RTN does.
  * ---------------------------------------------------------------------- */
 
-/* H = 2 X^T X in fp64 (products of bf16 values are exact). x: [t][k]. */
+/* H = 2 X^T X in fp64 (products of bf16 values are exact). x: [t][k].
+ * The columns of X are copied out first (xt[i][r] = X[r][i]) so that each
+ * sum runs over contiguous memory; the sums are the same, in the same order. */
 int oracle_gptq_hessian(const uint16_t *x, int64_t t, int64_t k, double *h)
 {
     if (t <= 0 || k <= 0) return -1;
+    double *xt = (double *)malloc(sizeof(double) * (size_t)(t * k));
+    if (!xt) return -1;
+    for (int64_t r = 0; r < t; ++r)
+        for (int64_t i = 0; i < k; ++i) xt[i * t + r] = (double)bf16_bits_to_f32(x[r * k + i]);
     for (int64_t i = 0; i < k; ++i)
         for (int64_t j = 0; j <= i; ++j) {
+            const double *a = xt + i * t, *b = xt + j * t;
             double acc = 0.0;
-            for (int64_t r = 0; r < t; ++r)
-                acc += (double)bf16_bits_to_f32(x[r * k + i]) * (double)bf16_bits_to_f32(x[r * k + j]);
+            for (int64_t r = 0; r < t; ++r) acc += a[r] * b[r];
             h[i * k + j] = h[j * k + i] = 2.0 * acc;
         }
+    free(xt);
     return 0;
 }
 
@@ -727,16 +734,20 @@ int oracle_gptq_inverse_factor(double *h, int64_t k, double percdamp, float *u)
             v[i * k + j] = s / vjj;
         }
     }
-    /* W = V^-1 (upper): back substitution, column by column */
+    /* W = V^-1 (upper): back substitution, column by column. Column c of W
+     * is kept as row c of wt (wt[c][m] = W[m][c]) so the sums run over
+     * contiguous memory. */
+    double *wt = w;
     for (int64_t c = 0; c < k; ++c) {
-        w[c * k + c] = 1.0 / v[c * k + c];
+        wt[c * k + c] = 1.0 / v[c * k + c];
         for (int64_t i = c - 1; i >= 0; --i) {
             double s = 0.0;
-            for (int64_t m = i + 1; m <= c; ++m) s += v[i * k + m] * w[m * k + c];
-            w[i * k + c] = -s / v[i * k + i];
+            for (int64_t m = i + 1; m <= c; ++m) s += v[i * k + m] * wt[c * k + m];
+            wt[c * k + i] = -s / v[i * k + i];
         }
     }
-    for (int64_t i = 0; i < k * k; ++i) u[i] = (float)w[i];
+    for (int64_t i = 0; i < k; ++i)
+        for (int64_t c = 0; c < k; ++c) u[i * k + c] = (float)wt[c * k + i];
     rc = 0;
 out:
     free(v);

@@ -140,6 +140,9 @@ def test_smoothquant_entry_points_reject(lib):
     assert lib.smooth_scale(A16, 8, B16, 8, 200, ctypes.c_float(0.5), C16, None) == 2
     assert lib.quant_per_token_int8(A16, 4, 256, P((7 << 20) + 8), B16, C16, None) == 1
     assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 131072 + 128, None, P(9 << 20), None) == 2
+    # k = 131072 with every code -128 would reach 2^31: rejected before any launch
+    assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 131072, None, P(9 << 20), None) == 2
+    assert b"130944" in lib.lq_last_error()
     assert lib.w8a8_gemm(A16, B16, 4, C16, D16, 4, 256, P(9 << 20), P(9 << 20), None) == 1
 
 
