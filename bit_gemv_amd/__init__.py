@@ -79,6 +79,10 @@ def load_library(path: Optional[str] = None):
     lib.awq_workspace_bytes.restype = ctypes.c_int64
     lib.gptq_workspace_bytes.argtypes = [I64, I64, I64]
     lib.gptq_workspace_bytes.restype = ctypes.c_int64
+    lib.lq_read_probe_sink_words.argtypes = []
+    lib.lq_read_probe_sink_words.restype = ctypes.c_int64
+    lib.lq_hbm_read_probe.argtypes = [P, I64, P, P]
+    lib.lq_hbm_read_probe.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -382,3 +386,15 @@ def gptq_quantize(w: torch.Tensor, u: torch.Tensor, bits: int = 4, symmetric: bo
     _call("gptq_quantize", _ptr(w), n, k, _ptr(u), bits, int(bool(symmetric)), group, _ptr(ws), ws.numel(),
           _ptr(codes), _ptr(scales), _ptr(zeros), _stream())
     return PackedWeight(codes, scales, zeros, n, k, bits, bool(symmetric), group)
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Streaming read of the whole (contiguous, 16-byte aligned) tensor with
+    the library's read-probe kernel; returns the sink it may write."""
+    lib = load_library()
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty(lib.lq_read_probe_sink_words(), dtype=torch.int32, device=buf.device)
+    _call("lq_hbm_read_probe", _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream())
+    return sink

@@ -458,3 +458,19 @@ lq_status awq_search(const void *x_bf16, int64_t t, const void *w_bf16, int64_t 
 }
 
 }  // extern "C"
+
+int64_t lq_read_probe_sink_words(void) { return lq::read_probe_sink_words(); }
+
+lq_status lq_hbm_read_probe(const void *p, int64_t bytes, uint32_t *sink, void *stream) {
+    const char *fn = "lq_hbm_read_probe";
+    if (bytes < 0 || bytes % 16 != 0) return fail(LQ_ERR_INVALID_ARG, "%s: bytes must be a non-negative multiple of 16", fn);
+    if (bytes > kMaxElems) return fail(LQ_ERR_UNSUPPORTED, "%s: buffer too large", fn);
+    if (bytes == 0) return LQ_OK;
+    if (!p || !aligned(p, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: buffer null or not 16-byte aligned", fn);
+    if (!sink || !aligned(sink, 4)) return fail(LQ_ERR_INVALID_ARG, "%s: sink null or misaligned", fn);
+    if (any_overlap({{sink, lq::read_probe_sink_words() * 4}}, {{p, bytes}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: the sink overlaps the buffer", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    return launched(lq::launch_read_probe(p, bytes, sink, static_cast<hipStream_t>(stream)), fn);
+}

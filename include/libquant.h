@@ -351,6 +351,21 @@ lq_status awq_search(const void *x_bf16, int64_t t, const void *w_bf16, int64_t 
                      int64_t workspace_bytes, float *s_best, double *losses, int32_t *best, void *codes,
                      float *scales, float *zeros, void *stream);
 
+/*
+ * Measurement helper (not a step of the method).
+ *
+ * lq_hbm_read_probe -- reads `bytes` bytes at `p` once with a streaming-read
+ * kernel and nothing else: the HBM read rate a kernel that only reads
+ * reaches on this device, the practical ceiling of the memory-bound kernels
+ * above ("3.6 Quantization": batch-1 decode time is the bytes read over the
+ * memory bandwidth). p: device buffer, 16-byte aligned; bytes a multiple of
+ * 16. sink: device scratch of lq_read_probe_sink_words() uint32 words that
+ * the kernel may write (its contents are meaningless). Asynchronous on
+ * `stream`; time it with events around the call.
+ */
+int64_t lq_read_probe_sink_words(void);
+lq_status lq_hbm_read_probe(const void *p, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

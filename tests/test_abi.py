@@ -244,3 +244,13 @@ def test_gptq_entry_points_reject(lib):
     assert q(n=0, w=None, codes=None) == 0
     if torch.cuda.device_count() == 0:
         assert f() == 4 and q() == 4
+
+
+def test_read_probe_rejects(lib):
+    lib.lq_hbm_read_probe.argtypes = [P, ctypes.c_int64, P, P]
+    assert lib.lq_read_probe_sink_words() == 1024
+    assert lib.lq_hbm_read_probe(A16, 0, B16, None) == 0          # empty: no-op
+    assert lib.lq_hbm_read_probe(A16, 24, B16, None) == 1         # not a multiple of 16
+    assert lib.lq_hbm_read_probe(MIS, 1024, B16, None) == 1       # misaligned buffer
+    assert lib.lq_hbm_read_probe(A16, 1024, None, None) == 1      # no sink
+    assert lib.lq_hbm_read_probe(A16, 1 << 20, P((1 << 20) + 64), None) == 1  # sink inside the buffer
