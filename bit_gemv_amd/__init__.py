@@ -64,6 +64,7 @@ def load_library(path: Optional[str] = None):
         "mxfp4_gemv": [P, I64, P, P, I64, I64, P, P],
         "gptq_hessian_factor": [P, I64, I64, F, P, I64, P, P],
         "gptq_quantize": [P, I64, I64, P, I, I, I64, P, I64, P, P, P, P],
+        "gptq_quantize_noalloc": [P, I64, I64, P, I, I, I64, P, P, P, P],
         "awq_search": [P, I64, P, I64, I64, I, I64, I, P, P, I64, P, P, P, P, P, P, P],
     }
     for name, argtypes in sigs.items():
@@ -79,6 +80,8 @@ def load_library(path: Optional[str] = None):
     lib.awq_workspace_bytes.restype = ctypes.c_int64
     lib.gptq_workspace_bytes.argtypes = [I64, I64, I64]
     lib.gptq_workspace_bytes.restype = ctypes.c_int64
+    lib.gptq_quantize_noalloc_max_bytes.argtypes = []
+    lib.gptq_quantize_noalloc_max_bytes.restype = ctypes.c_int64
     lib.lq_read_probe_sink_words.argtypes = []
     lib.lq_read_probe_sink_words.restype = ctypes.c_int64
     lib.lq_hbm_read_probe.argtypes = [P, I64, P, P]
@@ -398,3 +401,23 @@ def hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> to
         sink = torch.empty(lib.lq_read_probe_sink_words(), dtype=torch.int32, device=buf.device)
     _call("lq_hbm_read_probe", _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream())
     return sink
+
+
+def gptq_quantize_noalloc(w: torch.Tensor, u: torch.Tensor, bits: int = 4, symmetric: bool = False,
+                          group: int = 128, out: Optional[PackedWeight] = None) -> PackedWeight:
+    """gptq_quantize through the entry point without a workspace (its scratch
+    is the library's static device array). Outputs are allocated here when
+    not given; the C call itself allocates nothing."""
+    _need(w, "w", torch.bfloat16)
+    n, k = w.shape
+    _need(u, "u", torch.float32, (k, k))
+    if out is None:
+        dev = w.device
+        ng = k // group if group > 0 and k % group == 0 else 0
+        codes = torch.empty((n, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, ng), dtype=torch.float32, device=dev)
+        zeros = None if symmetric else torch.empty((n, ng), dtype=torch.float32, device=dev)
+        out = PackedWeight(codes, scales, zeros, n, k, bits, bool(symmetric), group)
+    _call("gptq_quantize_noalloc", _ptr(w), n, k, _ptr(u), bits, int(bool(symmetric)), group, _ptr(out.codes),
+          _ptr(out.scales), _ptr(out.zeros), _stream())
+    return out

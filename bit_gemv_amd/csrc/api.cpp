@@ -366,10 +366,12 @@ lq_status gptq_hessian_factor(const void *x_bf16, int64_t t, int64_t k, float pe
                     fn);
 }
 
-lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
-                        int64_t group, void *workspace, int64_t workspace_bytes, void *codes, float *scales,
-                        float *zeros, void *stream) {
-    const char *fn = "gptq_quantize";
+namespace {
+
+// Arguments of the column loop other than its scratch.
+lq_status check_gptq_quantize(const char *fn, const void *w_bf16, int64_t n, int64_t k, const float *u, int bits,
+                              int symmetric, int64_t group, const void *codes, const float *scales,
+                              const float *zeros) {
     if (n < 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative n", fn);
     lq_status st = check_group(fn, k, bits, group);
     if (st != LQ_OK) return st;
@@ -378,7 +380,17 @@ lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u
     if (!w_bf16 || !aligned(w_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: w null or not 16-byte aligned", fn);
     if (!u || !aligned(u, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: u null or not 16-byte aligned", fn);
     if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
-    if ((st = check_meta(fn, symmetric, scales, zeros)) != LQ_OK) return st;
+    return check_meta(fn, symmetric, scales, zeros);
+}
+
+}  // namespace
+
+lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                        int64_t group, void *workspace, int64_t workspace_bytes, void *codes, float *scales,
+                        float *zeros, void *stream) {
+    const char *fn = "gptq_quantize";
+    lq_status st = check_gptq_quantize(fn, w_bf16, n, k, u, bits, symmetric, group, codes, scales, zeros);
+    if (st != LQ_OK || n == 0) return st;
     const int64_t need = lq::gptq_quantize_workspace_bytes(n, k);
     if (!workspace || !aligned(workspace, 256))
         return fail(LQ_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
@@ -392,6 +404,37 @@ lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u
         return fail(LQ_ERR_INVALID_ARG, "%s: an output or the workspace overlaps an input or another output", fn);
     if ((st = need_device()) != LQ_OK) return st;
     lq::GptqArgs a{static_cast<const uint16_t *>(w_bf16), n, k, u, bits, symmetric, group, workspace,
+                   static_cast<uint8_t *>(codes), scales, zeros};
+    return launched(lq::launch_gptq_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int64_t gptq_quantize_noalloc_max_bytes(void) { return lq::gptq_static_scratch_bytes(); }
+
+lq_status gptq_quantize_noalloc(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                                int64_t group, void *codes, float *scales, float *zeros, void *stream) {
+    const char *fn = "gptq_quantize_noalloc";
+    lq_status st = check_gptq_quantize(fn, w_bf16, n, k, u, bits, symmetric, group, codes, scales, zeros);
+    if (st != LQ_OK || n == 0) return st;
+    const int64_t need = lq::gptq_quantize_workspace_bytes(n, k);
+    const int64_t have = lq::gptq_static_scratch_bytes();
+    if (need > have)
+        return fail(LQ_ERR_UNSUPPORTED,
+                    "%s: n = %lld, k = %lld needs %lld bytes of scratch (an fp32 copy of W and the block's "
+                    "scaled errors); the static scratch holds %lld. Use gptq_quantize with a workspace",
+                    fn, (long long)n, (long long)k, (long long)need, (long long)have);
+    const int64_t meta = n * (k / group) * 4;
+    const int64_t cbytes = bits == 4 ? n * k / 2 : n * k;
+    if (any_overlap({{codes, cbytes}, {scales, meta}, {zeros, symmetric ? 0 : meta}},
+                    {{w_bf16, n * k * 2}, {u, k * k * 4}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: an output overlaps an input or another output", fn);
+    if ((st = need_device()) != LQ_OK) return st;
+    void *ws = nullptr;
+    const hipError_t e = lq::gptq_static_scratch(&ws);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LQ_ERR_HIP, "%s: the static scratch's device address: %s", fn, hipGetErrorString(e));
+    }
+    lq::GptqArgs a{static_cast<const uint16_t *>(w_bf16), n, k, u, bits, symmetric, group, ws,
                    static_cast<uint8_t *>(codes), scales, zeros};
     return launched(lq::launch_gptq_quantize(a, static_cast<hipStream_t>(stream)), fn);
 }

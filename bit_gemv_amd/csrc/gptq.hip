@@ -31,6 +31,8 @@
 //    order with fused multiply-adds -- the same operations, in the same
 //    order, as applying each column's update as it is made.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -612,6 +614,43 @@ hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float per
         if ((e = mgemm_deep<false, true>(j0, NB, j0, -1.0f, u, k, tmp, NB, 0, u + j0, k, part, st)) != hipSuccess)
             return e;
     }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free column loop (gptq_quantize_noalloc): a
+// file-scope device array. Every device the library runs on holds its own
+// copy of it until the process ends. In host code the name `scratch` is only
+// a host-side stand-in for the symbol, so host code never passes it to a
+// kernel; it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+constexpr int64_t kStaticScratchBytes = int64_t(72) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+int64_t gptq_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t gptq_static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
     return hipSuccess;
 }
 

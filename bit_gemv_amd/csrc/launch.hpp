@@ -147,6 +147,10 @@ int64_t gptq_quantize_workspace_bytes(int64_t n, int64_t k);
 hipError_t launch_gptq_factor(const uint16_t *x, int64_t t, int64_t k, float percdamp, void *workspace, float *u,
                               hipStream_t st);
 hipError_t launch_gptq_quantize(const GptqArgs &a, hipStream_t st);
+// The column loop's static device scratch: its size, and its device address
+// on the current device (looked up once per device).
+int64_t gptq_static_scratch_bytes();
+hipError_t gptq_static_scratch(void **ptr);
 // Y[m][n] = A[m][k] B[n][k]^T, bf16 inputs (k a multiple of 64), fp32 out.
 hipError_t launch_gemm_bf16(const uint16_t *a, const uint16_t *b, int64_t m, int64_t n, int64_t k, float *y,
                             hipStream_t st);

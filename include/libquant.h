@@ -300,6 +300,25 @@ lq_status gptq_quantize(const void *w_bf16, int64_t n, int64_t k, const float *u
                         float *zeros, void *stream);
 
 /*
+ * gptq_quantize_noalloc -- gptq_quantize without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or quantization loops, harnesses that forbid
+ * hipMalloc. The call itself allocates and frees nothing. Its scratch (the
+ * fp32 copy of W and the block's scaled errors, n * k * 4 + n * 512 bytes,
+ * each part rounded up to 256) lives in a static device array of
+ * gptq_quantize_noalloc_max_bytes() bytes (72 MiB: one 4096 x 4096 linear
+ * fits) that every device the library runs on holds until the process ends;
+ * larger n * k return LQ_ERR_UNSUPPORTED before any work. Every call on a
+ * device uses that device's one array, so calls that overlap on one device
+ * (other streams, other threads) race; calls in order on one stream do not.
+ * The array keeps the last call's contents; nothing in it needs to start at
+ * zero. Arguments, outputs and errors otherwise as gptq_quantize.
+ */
+int64_t gptq_quantize_noalloc_max_bytes(void);
+lq_status gptq_quantize_noalloc(const void *w_bf16, int64_t n, int64_t k, const float *u, int bits, int symmetric,
+                                int64_t group, void *codes, float *scales, float *zeros, void *stream);
+
+/*
  * act_absmean -- the per-channel activation magnitude AWQ scales by
  * ("3.6 Quantization", AWQ section: s_X, the average activation magnitude of
  * each input channel over the calibration data; PTQ concept page, AWQ step 1):
