@@ -388,6 +388,23 @@ def measure_rows(dev, packed, shapes, names, wl, groups) -> dict:
         del pwq, x, y
     rows["w4a16_gemm_prefill"] = {"workload": pf.name, "m": pf.tokens, "bound": "mfma", "shapes": gem}
 
+    # f4: the same prefill shapes with MXFP4 weights (bf16 MFMA on exact E2M1 * 2^e operands)
+    gmx = {}
+    for i, lin in enumerate(pf.linears):
+        w = dev_bf16(pf.weight(0, i))
+        mwq = bg.mxfp4_quantize(w)
+        del w
+        x = dev_bf16(pf.activation(lin.k, pf.tokens))
+        y = torch.empty((pf.tokens, lin.n), dtype=torch.float32, device=dev)
+        ms = _timed(lambda: bg.mxfp4_gemm(x, mwq, y), reps=5)
+        tf = 2.0 * pf.tokens * lin.n * lin.k / (ms * 1e-3) / 1e12
+        gmx[f"{lin.name} {lin.n}x{lin.k}"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                                               "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] mxfp4_gemm M={pf.tokens} {lin.n}x{lin.k}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        del mwq, x, y
+    rows["mxfp4_gemm_prefill"] = {"workload": pf.name, "m": pf.tokens, "bound": "mfma",
+                                  "quant": "MXFP4 (E2M1, E8M0 scale per 32)", "shapes": gmx}
+
     # a8-a11: SmoothQuant W8A8, X 512 x 8192 with outlier channels, W 8192 x 8192
     sq = WORKLOADS["smoothquant"]
     lin = sq.linears[0]

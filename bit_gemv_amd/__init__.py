@@ -27,7 +27,7 @@ LQ_OK, LQ_ERR_INVALID_ARG, LQ_ERR_UNSUPPORTED, LQ_ERR_HIP, LQ_ERR_NO_DEVICE = ra
 
 ENTRY_POINTS = ("quantize_groupwise", "dequantize_groupwise", "w4a16_gemv", "w8a16_gemv", "w4a16_gemm",
                 "smooth_scale", "quant_per_token_int8", "w8a8_gemm", "act_absmean", "awq_search",
-                "mxfp4_quantize", "mxfp4_gemv", "gptq_hessian_factor", "gptq_quantize")
+                "mxfp4_quantize", "mxfp4_gemv", "mxfp4_gemm", "gptq_hessian_factor", "gptq_quantize")
 
 
 class LibquantError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: Optional[str] = None):
         "act_absmean": [P, I64, I64, P, P],
         "mxfp4_quantize": [P, I64, I64, P, P, P],
         "mxfp4_gemv": [P, I64, P, P, I64, I64, P, P],
+        "mxfp4_gemm": [P, I64, P, P, I64, I64, P, P],
         "gptq_hessian_factor": [P, I64, I64, F, P, I64, P, P],
         "gptq_quantize": [P, I64, I64, P, I, I, I64, P, I64, P, P, P, P],
         "gptq_quantize_noalloc": [P, I64, I64, P, I, I, I64, P, P, P, P],
@@ -347,6 +348,19 @@ def mxfp4_gemv(x: torch.Tensor, mw: MxWeight, y: Optional[torch.Tensor] = None) 
         y = torch.empty((m, mw.n), dtype=torch.float32, device=x.device)
     _need(y, "y", torch.float32, (m, mw.n))
     _call("mxfp4_gemv", _ptr(x), m, _ptr(mw.codes), _ptr(mw.scales), mw.n, mw.k, _ptr(y), _stream())
+    return y
+
+
+def mxfp4_gemm(x: torch.Tensor, mw: MxWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W^T with MXFP4 weights, x bf16 [m][k], any m (prefill)."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    if k != mw.k:
+        raise ValueError(f"x has {k} columns, weights have k = {mw.k}")
+    if y is None:
+        y = torch.empty((m, mw.n), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, mw.n))
+    _call("mxfp4_gemm", _ptr(x), m, _ptr(mw.codes), _ptr(mw.scales), mw.n, mw.k, _ptr(y), _stream())
     return y
 
 

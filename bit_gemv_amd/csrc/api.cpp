@@ -332,6 +332,29 @@ lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const voi
     return launched(lq::launch_mx_gemv(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+lq_status mxfp4_gemm(const void *x_bf16, int64_t m, const void *codes, const void *scales, int64_t n, int64_t k,
+                     float *y, void *stream) {
+    const char *fn = "mxfp4_gemm";
+    if (m < 0 || n < 0 || k <= 0) return fail(LQ_ERR_INVALID_ARG, "%s: negative size or k <= 0", fn);
+    if (k % 32 != 0) return fail(LQ_ERR_INVALID_ARG, "%s: k (%lld) is not a multiple of the block of 32", fn,
+                                 (long long)k);
+    if (k % 128 != 0) return fail(LQ_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+    if (m > kMaxDim || n > kMaxDim || k >= (int64_t(1) << 24))
+        return fail(LQ_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    if (m == 0 || n == 0) return LQ_OK;
+    if (!x_bf16 || !aligned(x_bf16, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: x null or not 16-byte aligned", fn);
+    if (!codes || !aligned(codes, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: codes null or not 16-byte aligned", fn);
+    if (!scales || !aligned(scales, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: scales null or not 16-byte aligned", fn);
+    if (!y || !aligned(y, 16)) return fail(LQ_ERR_INVALID_ARG, "%s: y null or not 16-byte aligned", fn);
+    if (any_overlap({{y, m * n * 4}}, {{x_bf16, m * k * 2}, {codes, n * k / 2}, {scales, n * k / 32}}))
+        return fail(LQ_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    lq_status st;
+    if ((st = need_device()) != LQ_OK) return st;
+    lq::MxArgs a{static_cast<const uint16_t *>(x_bf16), m, static_cast<const uint8_t *>(codes),
+                 static_cast<const uint8_t *>(scales), n, k, y};
+    return launched(lq::launch_mxfp4_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 int64_t gptq_workspace_bytes(int64_t t, int64_t n, int64_t k) {
     if (t < 0 || n < 0 || k <= 0 || t > kMaxDim || n > kMaxDim || k > kMaxDim || k * k > kMaxElems ||
         n * k > kMaxElems || t * k > kMaxElems)

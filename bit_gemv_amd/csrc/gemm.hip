@@ -26,6 +26,15 @@
 // fragment load hit distinct banks.
 // Blocks are mapped XCD-aware: the hardware deals block b to XCD b % 8, and
 // the blocks that share a 128-column slice of the codes are put on one XCD.
+//
+// MXFP4 weights (gemm_mx_kernel; "3.6 Quantization", number-format table:
+// FP4 E2M1 elements in blocks of 32 sharing an E8M0 power-of-two scale):
+//   Y[m][n] = sum_j X[m][j] E2M1(c[n][j]) 2^e[n][j/32].
+// The same tiles, ring and fragment layout; a lane's 32 k of a column in one
+// step are exactly one block of 32, so v_cvt_scalef32_pk_bf16_fp4 with the
+// block's 2^e turns each code byte into the exact bf16 pair E2M1(c) 2^e and
+// the MFMAs accumulate Y directly: no zero point, no activation sums, no
+// per-step correction. The step's 4 scale bytes of a column are one dword.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -284,7 +293,149 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     }
 }
 
+__global__ __launch_bounds__(256) void gemm_mx_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales, float *__restrict__ y) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l16 = lane & 15, kq = lane >> 4;
+
+    const int nt_count = (n + BN - 1) / BN, mt_count = (m + BM - 1) / BM;
+    int tn, tm;
+    if ((nt_count & 7) == 0) {
+        const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+        tn = xcd * (nt_count >> 3) + idx / mt_count;
+        tm = idx % mt_count;
+    } else {
+        tn = blockIdx.x % nt_count;
+        tm = blockIdx.x / nt_count;
+    }
+    const int n0 = tn * BN, m0 = tm * BM;
+    const int ngroups = k / GK;
+    const uint32_t srow = (uint32_t)k / 32;  // scale bytes per row
+
+    const int rows_m = min(BM, m - m0), rows_n = min(BN, n - n0);
+    const uint32_t row_bytes = (uint32_t)k / 2;
+    const auto rx = make_rsrc(x + (int64_t)m0 * k, (uint32_t)rows_m * (uint32_t)k * 2);
+    const auto rc = make_rsrc(codes + (int64_t)n0 * row_bytes, (uint32_t)rows_n * row_bytes);
+    const auto rs = make_rsrc(scales + (int64_t)n0 * srow, (uint32_t)rows_n * srow);
+
+    // the same 1 KB pieces as the INT4 kernel (activation rows, code columns)
+    uint32_t src_off[kPiecesPerWave];
+#pragma unroll
+    for (int i = 0; i < kPiecesPerWave; ++i) {
+        const int q = kPiecesPerWave * wave + i;
+        if (q < kXBytes / 1024) {
+            const int row = 4 * q + (lane >> 4);
+            src_off[i] = (uint32_t)row * (uint32_t)k * 2 + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+        } else {
+            const int col = 16 * (q - kXBytes / 1024) + (lane >> 2);
+            src_off[i] = (uint32_t)col * row_bytes + 16u * (uint32_t)((lane & 3) ^ swz(col));
+        }
+    }
+    auto issue = [&](int g) {
+        uint8_t *slot = ring[g % kStages];
+        const bool in = g < ngroups;
+#pragma unroll
+        for (int i = 0; i < kPiecesPerWave; ++i) {
+            const int q = kPiecesPerWave * wave + i;
+            const bool is_x = q < kXBytes / 1024;
+            const uint32_t step_bytes = is_x ? GK * 2 : GK / 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_x ? rx : rc,
+                                                     (__attribute__((address_space(3))) void *)(slot + 1024 * q), 16,
+                                                     in ? src_off[i] + (uint32_t)g * step_bytes : kOutOfRange, 0, 0,
+                                                     0);
+        }
+        // the step's 4 scale bytes of columns 64 (wave & 1) + lane (waves 0, 1);
+        // waves 2, 3 issue an empty load so every wave counts the same loads
+        const uint32_t so = (uint32_t)(64 * (wave & 1) + lane) * srow + (uint32_t)g * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(slot + kSZOff + 256 * wave),
+                                                 4, in && wave < 2 ? so : kOutOfRange, 0, 0, 0);
+    };
+
+    int a_off[4][4], c_off[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            a_off[mt][j] = (wm * 64 + mt * 16 + l16) * (GK * 2) + 16 * ((4 * kq + j) ^ l16);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int col = wn * 64 + nt * 16 + l16;
+        c_off[nt] = kXBytes + col * (GK / 2) + 16 * (kq ^ swz(col));
+    }
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s);
+    for (int g = 0; g < ngroups; ++g) {
+        asm volatile("s_waitcnt vmcnt(" LQ_GEMM_STR(LQ_GEMM_VM_STEP) ")\n\ts_barrier" ::: "memory");
+        issue(g + kStages - 1);
+
+        const uint8_t *slot = ring[g % kStages];
+        // this lane's block of 32 in column col is block kq of the step:
+        // 2^(e - 127) from the E8M0 byte in the fp32 exponent field (the
+        // byte 0, +0.0f, acts as 2^-127 in the scaled conversion)
+        float scale[4];
+        u32x4 cw[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int col = wn * 64 + nt * 16 + l16;
+            const uint32_t e8 = slot[kSZOff + 256 * (col >> 6) + 4 * (col & 63) + kq];
+            scale[nt] = __uint_as_float(e8 << 23);
+            cw[nt] = *reinterpret_cast<const u32x4 *>(slot + c_off[nt]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t bop[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t w = j == 0 ? cw[nt].x : j == 1 ? cw[nt].y : j == 2 ? cw[nt].z : cw[nt].w;
+                u32x4 p;
+                p.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale[nt], 0));
+                p.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale[nt], 1));
+                p.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale[nt], 2));
+                p.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale[nt], 3));
+                bop[nt] = __builtin_bit_cast(bf16x8_t, p);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8_t aop = *reinterpret_cast<const bf16x8_t *>(slot + a_off[mt][j]);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm * 64 + mt * 16 + kq * 4 + v;
+                const int col = n0 + wn * 64 + nt * 16 + l16;
+                if (row < m && col < n) y[(int64_t)row * n + col] = acc[mt][nt][v];
+            }
+}
+
 }  // namespace
+
+hipError_t launch_mxfp4_gemm(const MxArgs &a, hipStream_t st) {
+    const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
+    hipLaunchKernelGGL(gemm_mx_kernel, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k, a.codes,
+                       a.scales, a.y);
+    return hipGetLastError();
+}
 
 hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st) {
     const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));

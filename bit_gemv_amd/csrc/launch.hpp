@@ -160,6 +160,9 @@ int64_t awq_workspace_bytes(int64_t t, int64_t n, int64_t k);
 bool shared_gemv_pays(WeightFormat f, int64_t m, int64_t n, int64_t k);
 hipError_t launch_shared_gemv(WeightFormat f, const SharedGemvArgs &a, hipStream_t st);
 
+// MXFP4 prefill GEMM (gemm.hip): Y[m][n] = X W^T with MXFP4 weights, any m.
+hipError_t launch_mxfp4_gemm(const MxArgs &a, hipStream_t st);
+
 // streaming-read probe (probe.hip)
 int64_t read_probe_sink_words();
 hipError_t launch_read_probe(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st);

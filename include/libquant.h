@@ -255,6 +255,24 @@ lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const voi
                      int64_t n, int64_t k, float *y, void *stream);
 
 /*
+ * mxfp4_gemm -- prefill-shaped product with MXFP4 weights and 16-bit
+ * activations, same definition as mxfp4_gemv for any m ("3.6 Quantization",
+ * number-format table: MXFP4 is FP4 E2M1 elements in blocks of 32 sharing an
+ * E8M0 scale, aimed at 4-bit matrix-core GEMMs; "LLM quantization deep
+ * dive", prefill is compute-bound):
+ *   y[i][r] = sum_j x[i][j] * E2M1(c[r][j]) * 2^(scales[r][j/32] - 127)
+ * Runs on bf16 MFMA: each code byte with its block's scale converts to the
+ * exact bf16 pair E2M1(c) 2^e, so the products are exact and the sums fp32.
+ * x_bf16 [m][k]; codes, scales as mxfp4_quantize writes them; y out fp32
+ * [m][n]. 16-byte aligned; k a multiple of 128 and below 2^24 (a multiple of
+ * 32 that is not a multiple of 128: LQ_ERR_UNSUPPORTED; not a multiple of
+ * 32: LQ_ERR_INVALID_ARG). E2M1(c) 2^e above the bf16 range (code 6 with
+ * e = 127) gives inf, as the exact result would.
+ */
+lq_status mxfp4_gemm(const void *x_bf16, int64_t m, const void *codes, const void *scales, int64_t n, int64_t k,
+                     float *y, void *stream);
+
+/*
  * gptq_workspace_bytes -- device workspace gptq_hessian_factor (t tokens, k
  * channels) and gptq_quantize (n rows, k columns) need; the larger of the
  * two (pass t = 0 or n = 0 for one of them). -1 for sizes they would reject.

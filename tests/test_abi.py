@@ -254,3 +254,13 @@ def test_read_probe_rejects(lib):
     assert lib.lq_hbm_read_probe(MIS, 1024, B16, None) == 1       # misaligned buffer
     assert lib.lq_hbm_read_probe(A16, 1024, None, None) == 1      # no sink
     assert lib.lq_hbm_read_probe(A16, 1 << 20, P((1 << 20) + 64), None) == 1  # sink inside the buffer
+
+
+def test_mxfp4_gemm_rejects(lib):
+    assert lib.mxfp4_gemm(A16, 0, B16, C16, 8, 256, D16, None) == 0          # m = 0: no-op
+    assert lib.mxfp4_gemm(A16, 4, B16, C16, 8, 100, D16, None) == 1          # k not a multiple of 32
+    assert lib.mxfp4_gemm(A16, 4, B16, C16, 8, 160, D16, None) == 2          # multiple of 32, not of 128
+    assert lib.mxfp4_gemm(A16, 4, B16, C16, 8, 1 << 24, D16, None) == 2      # k too large
+    assert lib.mxfp4_gemm(MIS, 4, B16, C16, 8, 256, D16, None) == 1          # misaligned x
+    assert lib.mxfp4_gemm(A16, 4, B16, C16, 8, 256, MIS, None) == 1          # misaligned y
+    assert lib.mxfp4_gemm(A16, 4, B16, C16, 8, 256, P((1 << 20) + 256), None) == 1  # y overlaps x

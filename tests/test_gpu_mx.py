@@ -149,3 +149,107 @@ def test_shared_stage_row_magnitudes(b):
     say(f"  worst |y - y_ref| / sum|x w| = {worst:.2e}")
     assert np.all(np.isfinite(y))
     assert np.all(err <= 1e-4 * bound), worst
+
+
+# --------------------------------------------------------------------------
+# MXFP4 prefill GEMM (bf16 MFMA on E2M1 * 2^e operands converted exactly)
+
+def _gemm_case(m, n, k, seed, w_scale=None, x_mult=None, what=""):
+    rng = np.random.default_rng(seed)
+    wf = rng.standard_normal((n, k)) * 0.02
+    if w_scale is not None:
+        wf = wf * w_scale
+    w = f32_to_bf16_bits(wf)
+    xf = rng.standard_normal((m, k))
+    if x_mult is not None:
+        xf = xf * x_mult
+    x = f32_to_bf16_bits(xf)
+    mw, c_ref, s_ref = _quant_check(w, f"gemm {what}")
+    say(f"mxfp4_gemm m={m} n={n} k={k} {what}")
+    y = host(bg.mxfp4_gemm(dev_bf16(x), mw))
+    y_ref = oracle.mx_matmul(x, c_ref, s_ref, n, k)
+    assert_close(y, y_ref, f"mx gemm m={m} n={n} k={k} {what}")
+    return y, y_ref
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 33, 384), (64, 200, 1024), (130, 130, 2048 + 128),
+                                   (257, 96, 4096), (128, 128, 128), (300, 1030, 2048)])
+def test_gemm_shapes(m, n, k):
+    """Single and several 128 x 128 tiles, ragged rows and columns (partial
+    tiles whose loads read zeros), one to 32 steps of k, n a multiple of
+    8 tiles (the XCD-grouped tile order) and not."""
+    _gemm_case(m, n, k, seed=m + n + k)
+
+
+def test_gemm_outlier_channels():
+    k = 2048
+    mult = np.ones(k)
+    mult[[3, 500, 1500, 2047]] = [20.0, 35.0, 50.0, 60.0]
+    _gemm_case(200, 144, k, seed=9, x_mult=mult, what="outliers")
+
+
+def test_gemm_row_magnitudes():
+    """Rows of W scaled by 2^-130 .. 2^90: block scales over most of the E8M0
+    range, with bf16-subnormal operands at the low end (the scaled conversion
+    and the MFMA keep them). Each output is checked against its own
+    magnitude, sum_j |x_j w_hat_j|."""
+    m, n, k = 70, 1000 + 3, 1024
+    rng = np.random.default_rng(77)
+    e = rng.integers(-130, 91, n)
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * np.ldexp(1.0, e)[:, None])
+    x = f32_to_bf16_bits(rng.standard_normal((m, k)))
+    mw, c_ref, s_ref = _quant_check(w, "gemm row magnitudes")
+    say(f"mxfp4_gemm row magnitudes m={m} n={n} k={k}")
+    y = host(bg.mxfp4_gemm(dev_bf16(x), mw)).astype(np.float64)
+    y_ref = oracle.mx_matmul(x, c_ref, s_ref, n, k)
+    from workloads import bf16_bits_to_f32
+    bound = np.abs(bf16_bits_to_f32(x).astype(np.float64)) @ np.abs(oracle.mx_dequantize(c_ref, s_ref, n, k)).T
+    err = np.abs(y - y_ref)
+    worst = float(np.max(err / np.where(bound > 0, bound, 1.0)))
+    say(f"  worst |y - y_ref| / sum|x w| = {worst:.2e}")
+    assert np.all(np.isfinite(y))
+    assert np.all(err <= 1e-4 * bound), worst
+
+
+def test_gemv_and_gemm_agree():
+    rng = np.random.default_rng(12)
+    n, k = 300, 4096
+    w = f32_to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    x = f32_to_bf16_bits(rng.standard_normal((16, k)))
+    mw = bg.mxfp4_quantize(dev_bf16(w))
+    yv = host(bg.mxfp4_gemv(dev_bf16(x), mw))
+    ym = host(bg.mxfp4_gemm(dev_bf16(x), mw))
+    assert np.abs(yv - ym).max() <= 1e-4 * np.abs(ym).max()
+
+
+def test_gemm_k_not_a_multiple_of_128_is_unsupported():
+    import torch
+    # a 160-wide MXFP4 weight (5 blocks of 32): valid MX, not a k this GEMM takes
+    mw = bg.MxWeight(torch.zeros((8, 80), dtype=torch.uint8, device="cuda"),
+                     torch.zeros((8, 5), dtype=torch.uint8, device="cuda"), 8, 160)
+    with pytest.raises(bg.LibquantError) as e:
+        bg.mxfp4_gemm(torch.zeros((4, 160), dtype=torch.bfloat16, device="cuda"), mw)
+    assert e.value.status == bg.LQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_gemm_prefill_workload_sampled(idx):
+    """The M = 2048 prefill shapes (8192 x 8192, 28672 x 8192, 8192 x 28672)
+    at full size with the workload's outlier activations; outputs on a
+    seeded sample of rows and columns against the oracle, and all finite."""
+    pf = WORKLOADS["prefill70b"]
+    lin = pf.linears[idx]
+    say(f"mxfp4_gemm prefill70b {lin.name} {lin.n}x{lin.k} M={pf.tokens}")
+    w = pf.weight(0, idx)
+    x = pf.activation(lin.k, pf.tokens)
+    mw = bg.mxfp4_quantize(dev_bf16(w))
+    y = host(bg.mxfp4_gemm(dev_bf16(x), mw))
+    rng = np.random.default_rng(200 + idx)
+    rows = np.sort(rng.choice(pf.tokens, 24, replace=False))
+    cols = np.sort(rng.choice(lin.n, 48, replace=False))
+    c_ref, s_ref = oracle.mx_quantize(w[cols])
+    assert_same_bits(host(mw.codes)[cols], c_ref, "codes (sampled rows)")
+    assert_same_bits(host(mw.scales)[cols], s_ref, "scales (sampled rows)")
+    y_ref = oracle.mx_matmul(x[rows], c_ref, s_ref, cols.size, lin.k)
+    assert_close(y[np.ix_(rows, cols)], y_ref, f"mx prefill {lin.name} sampled")
+    assert np.all(np.isfinite(y))
