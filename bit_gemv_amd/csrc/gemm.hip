@@ -13,19 +13,22 @@
 //    the same lane layout as D_g);
 //  * the fp32 correction acc += s (D_g - (128 + z) X_g) applies scale and
 //    zero point exactly once per group; no weight is ever rounded to bf16.
-// Tiles: a block of 4 waves computes 128 x 128 outputs (2 x 2 waves of
+// Tiles: a block of 8 waves computes 128 x 256 outputs (2 x 4 waves of
 // 64 x 64 = 4 x 4 MFMA tiles of 16 x 16) and walks k one 128-wide group per
-// step. A step's 128 x 128 activation tile (32 KB) and the 128 columns' code
-// words (8 KB) go straight from memory into one slot of an LDS ring (buffer
+// step. A step's 128 x 128 activation tile (32 KB) and the 256 columns' code
+// words (16 KB) go straight from memory into one slot of an LDS ring (buffer
 // loads with the LDS-write form, 16 bytes a lane), kStages - 1 steps ahead;
-// so do the 128 columns' scales and zeros of the step's group (one 4-byte
-// load form per wave: waves 0, 1 scales, waves 2, 3 zeros).
+// so do the 256 columns' scales and zeros of the step's group (one 4-byte
+// load form per wave: waves 0..3 scales, waves 4..7 zeros). Three slots of
+// 50 KB leave room for one block per CU, i.e. two waves per SIMD, so one
+// wave's unpacking and correction run while the other's MFMAs do (128 x 128
+// blocks of 4 waves, one per SIMD: 22-29 % slower on the M = 2048 shapes).
 // LDS slot layout: activation rows of 256 bytes whose sixteen 16-byte chunks
 // are XOR-permuted by (row & 15), then code columns of 64 bytes whose four
 // chunks are XOR-permuted by swz(col): the 16 rows (columns) read by one
 // fragment load hit distinct banks.
 // Blocks are mapped XCD-aware: the hardware deals block b to XCD b % 8, and
-// the blocks that share a 128-column slice of the codes are put on one XCD.
+// the blocks that share a 256-column slice of the codes are put on one XCD.
 //
 // MXFP4 weights (gemm_mx_kernel; "3.6 Quantization", number-format table:
 // FP4 E2M1 elements in blocks of 32 sharing an E8M0 power-of-two scale):
@@ -44,16 +47,17 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128, BN = 128, GK = 128;  // block tile and group width
+constexpr int BM = 128, BN = 256, GK = 128;  // block tile and group width
+constexpr int kWaves = BN / 32;               // 2 x 4 waves of 64 x 64 outputs
 constexpr int kStages = 3;                    // LDS ring depth
 constexpr int kXBytes = BM * GK * 2;          // activation tile of a step
 constexpr int kCBytes = BN * GK / 2;          // code tile of a step
 constexpr int kSZOff = kXBytes + kCBytes;     // then 128 scales and 128 zeros (fp32)
 constexpr int kSlot = kSZOff + 2 * BN * 4;
-constexpr int kPiecesPerWave = (kXBytes + kCBytes) / 1024 / 4;  // 16-byte loads per wave per step
+constexpr int kPiecesPerWave = (kXBytes + kCBytes) / 1024 / kWaves;  // 16-byte loads per wave per step
 constexpr int kLoadsPerWave = kPiecesPerWave + 1;               // and one 4-byte load (scales or zeros)
 // vmcnt literal pasted into the step barrier: (kStages - 2) steps of loads
-#define LQ_GEMM_VM_STEP 11
+#define LQ_GEMM_VM_STEP 7
 static_assert(LQ_GEMM_VM_STEP == (kStages - 2) * kLoadsPerWave, "step barrier vmcnt");
 
 constexpr uint32_t kMagicPair = 0x43004300u;  // bf16 pair (128, 128)
@@ -78,13 +82,13 @@ struct GemmBatch {
 };
 
 template <bool SYM, bool LOSS>
-__global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
+__global__ __launch_bounds__(512) void gemm_w4_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
                                                        const uint8_t *__restrict__ codes,
                                                        const float *__restrict__ scales,
                                                        const float *__restrict__ zeros, int group,
                                                        float *__restrict__ y, GemmBatch batch) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
-    __shared__ double wave_loss[4];
+    __shared__ double wave_loss[kWaves];
     x += (int64_t)blockIdx.y * batch.x_stride;
     codes += (int64_t)blockIdx.y * batch.code_stride;
     scales += (int64_t)blockIdx.y * batch.meta_stride;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int l16 = lane & 15, kq = lane >> 4;
 
     // tile of this block
@@ -154,11 +158,11 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
                                                      in ? src_off[i] + (uint32_t)g * step_bytes : kOutOfRange, 0, 0,
                                                      0);
         }
-        // scales (waves 0, 1) or zeros (waves 2, 3) of the group, columns
-        // 64 (wave & 1) + lane; no zeros when symmetric: an empty range
+        // scales (waves 0..3) or zeros (waves 4..7) of the group, columns
+        // 64 (wave & 3) + lane; no zeros when symmetric: an empty range
         const uint32_t gi = (uint32_t)((g * GK) / group);
-        const uint32_t so = (uint32_t)((64 * (wave & 1) + lane) * ng) * 4 + gi * 4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? rs : rz,
+        const uint32_t so = (uint32_t)((64 * (wave & 3) + lane) * ng) * 4 + gi * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? rs : rz,
                                                  (__attribute__((address_space(3))) void *)(slot + kSZOff + 256 * wave),
                                                  4, in ? so : kOutOfRange, 0, 0, 0);
     };
@@ -278,7 +282,9 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
         __syncthreads();
         if (tid == 0)
             batch.loss[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] =
-                ((wave_loss[0] + wave_loss[1]) + wave_loss[2]) + wave_loss[3];
+                ((((((wave_loss[0] + wave_loss[1]) + wave_loss[2]) + wave_loss[3]) + wave_loss[4]) + wave_loss[5]) +
+                 wave_loss[6]) +
+                wave_loss[7];
     } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -293,14 +299,14 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(const uint16_t *__restrict
     }
 }
 
-__global__ __launch_bounds__(256) void gemm_mx_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
+__global__ __launch_bounds__(512) void gemm_mx_kernel(const uint16_t *__restrict__ x, int m, int n, int k,
                                                       const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales, float *__restrict__ y) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int l16 = lane & 15, kq = lane >> 4;
 
     const int nt_count = (n + BN - 1) / BN, mt_count = (m + BM - 1) / BM;
@@ -349,11 +355,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint16_t *__restrict
                                                      in ? src_off[i] + (uint32_t)g * step_bytes : kOutOfRange, 0, 0,
                                                      0);
         }
-        // the step's 4 scale bytes of columns 64 (wave & 1) + lane (waves 0, 1);
-        // waves 2, 3 issue an empty load so every wave counts the same loads
-        const uint32_t so = (uint32_t)(64 * (wave & 1) + lane) * srow + (uint32_t)g * 4;
+        // the step's 4 scale bytes of columns 64 (wave & 3) + lane (waves 0..3);
+        // waves 4..7 issue an empty load so every wave counts the same loads
+        const uint32_t so = (uint32_t)(64 * (wave & 3) + lane) * srow + (uint32_t)g * 4;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(slot + kSZOff + 256 * wave),
-                                                 4, in && wave < 2 ? so : kOutOfRange, 0, 0, 0);
+                                                 4, in && wave < 4 ? so : kOutOfRange, 0, 0, 0);
     };
 
     int a_off[4][4], c_off[4];
@@ -432,7 +438,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint16_t *__restrict
 
 hipError_t launch_mxfp4_gemm(const MxArgs &a, hipStream_t st) {
     const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
-    hipLaunchKernelGGL(gemm_mx_kernel, dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k, a.codes,
+    hipLaunchKernelGGL(gemm_mx_kernel, dim3(blocks), dim3(512), 0, st, a.x, (int)a.m, (int)a.n, (int)a.k, a.codes,
                        a.scales, a.y);
     return hipGetLastError();
 }
@@ -441,10 +447,10 @@ hipError_t launch_w4a16_gemm(const WoArgs &a, hipStream_t st) {
     const uint32_t blocks = (uint32_t)(((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM));
     const GemmBatch one{0, 0, 0, nullptr, nullptr};
     if (a.symmetric)
-        hipLaunchKernelGGL((gemm_w4_kernel<true, false>), dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
+        hipLaunchKernelGGL((gemm_w4_kernel<true, false>), dim3(blocks), dim3(512), 0, st, a.x, (int)a.m, (int)a.n,
                            (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, one);
     else
-        hipLaunchKernelGGL((gemm_w4_kernel<false, false>), dim3(blocks), dim3(256), 0, st, a.x, (int)a.m, (int)a.n,
+        hipLaunchKernelGGL((gemm_w4_kernel<false, false>), dim3(blocks), dim3(512), 0, st, a.x, (int)a.m, (int)a.n,
                            (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, one);
     return hipGetLastError();
 }
@@ -456,10 +462,10 @@ hipError_t launch_w4a16_gemm_loss(const WoArgs &a, int points, int64_t x_stride,
     const uint32_t blocks = (uint32_t)w4a16_gemm_blocks(a.m, a.n);
     const GemmBatch b{x_stride, code_stride, meta_stride, yref, loss};
     if (a.symmetric)
-        hipLaunchKernelGGL((gemm_w4_kernel<true, true>), dim3(blocks, (uint32_t)points), dim3(256), 0, st, a.x,
+        hipLaunchKernelGGL((gemm_w4_kernel<true, true>), dim3(blocks, (uint32_t)points), dim3(512), 0, st, a.x,
                            (int)a.m, (int)a.n, (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, b);
     else
-        hipLaunchKernelGGL((gemm_w4_kernel<false, true>), dim3(blocks, (uint32_t)points), dim3(256), 0, st, a.x,
+        hipLaunchKernelGGL((gemm_w4_kernel<false, true>), dim3(blocks, (uint32_t)points), dim3(512), 0, st, a.x,
                            (int)a.m, (int)a.n, (int)a.k, a.codes, a.scales, a.zeros, (int)a.group, a.y, b);
     return hipGetLastError();
 }
