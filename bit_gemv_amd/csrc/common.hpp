@@ -80,6 +80,21 @@ LQ_DEVICE u32x4 unpack_natural(uint32_t w, uint32_t magic) {
     return p;
 }
 
+// fp32 quotient a / b from y = RN(1 / b) and FMA corrections (Markstein's
+// division; Muller et al., Handbook of Floating-Point Arithmetic, division
+// with a fused multiply-add): the first correction leaves q1 within one ulp
+// of a / b, and for such a q1 the step RN(q1 + (a - b q1) y), with the
+// residual exact, is RN(a / b), the IEEE quotient. That holds while every
+// intermediate is normal and finite; each caller states why its operands
+// qualify.
+LQ_DEVICE float div_rn(float a, float b, float y) {
+    const float q0 = a * y;
+    const float r0 = __builtin_fmaf(-q0, b, a);
+    const float q1 = __builtin_fmaf(r0, y, q0);
+    const float r1 = __builtin_fmaf(-q1, b, a);
+    return __builtin_fmaf(r1, y, q1);
+}
+
 // Workgroup barrier ordering LDS accesses only. __syncthreads() also
 // releases global memory, which makes each wave wait for all of its
 // outstanding global loads; this one leaves prefetches in flight.

@@ -65,26 +65,15 @@ LQ_DEVICE int code_of_quotient(float qd, float z) {
     }
 }
 
-// fp32 quotient a / b from y = RN(1 / b) and FMA corrections (Markstein's
-// division; Muller et al., Handbook of Floating-Point Arithmetic, division
-// with a fused multiply-add): the first correction leaves q1 within one ulp
-// of a / b, and for such a q1 the step RN(q1 + (a - b q1) y), with the
-// residual exact, is RN(a / b), the IEEE quotient. That holds while every
-// intermediate is normal and finite. The fast path of a group (magnitudes at
-// most 2^59) uses it for
+// Quotients through div_rn (common.hpp; Markstein's division): it equals the
+// IEEE quotient while every intermediate is normal and finite. The fast
+// path of a group (magnitudes at most 2^59) uses it for
 //  * the scale, range or absmax (at least 1e-8) over the level count: all
 //    intermediates are at least about 1e-8 * 2^-24, hence normal;
 //  * quotients that are then rounded to an integer, with divisor s in
 //    [1e-8 / 255, 2^60 / 7]: a quotient of magnitude 1/2 or more has
 //    |a| >= s / 2, so its residual is normal too; smaller ones round to
 //    zero under either path.
-LQ_DEVICE float div_rn(float a, float b, float y) {
-    const float q0 = a * y;
-    const float r0 = __builtin_fmaf(-q0, b, a);
-    const float q1 = __builtin_fmaf(r0, y, q0);
-    const float r1 = __builtin_fmaf(-q1, b, a);
-    return __builtin_fmaf(r1, y, q1);
-}
 
 // Fast path of a group: every magnitude at most 2^59. Then s lies in
 // [1e-8 / 255, 2^60 / 7] (range or absmax floored at 1e-8), every quotient

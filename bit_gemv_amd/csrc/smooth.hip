@@ -192,6 +192,12 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
     for (int i = 1; i < kWaves; ++i) a = fmaxf(a, red[i]);
     const float am = a < kFloor ? kFloor : a;
     const float s = am / 127.0f;
+    // X' / s through div_rn with y = RN(1 / s), once per token. It is the
+    // IEEE quotient here: |X'| <= am = 127 s (finite), s >= 1e-8 / 127 and
+    // y <= 1.3e10 are normal, and a quotient of magnitude 1/2 or more has
+    // |X'| >= s / 2, so its residuals are normal as well; smaller quotients
+    // round to 0 under either division.
+    const float y = 1.0f / s;
     // the last chunk is still in f; the others are read again
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
         if (ch != nch - 1) token_chunk<TPB, SM>(xr, smooth, k, ch * kTokChunk, t, f);
@@ -199,16 +205,19 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
         for (int i = 0; i < kTokLoads; ++i) {
             const int64_t e = ch * kTokChunk + t * 8 + 8 * TPB * i;
             if (e >= k) continue;
+            // q + 128 in 1 .. 255 is an exact small integer in a float:
+            // v_cvt_pk_u8_f32 places its byte, and xor 0x80 turns q + 128
+            // into the two's-complement byte of q
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int q = (int)clamp_code(rintf(f[i][j] / s), -127.0f, 127.0f);
+                const float q = clamp_code(rintf(div_rn(f[i][j], s, y)), -127.0f, 127.0f) + 128.0f;
                 if (j < 4)
-                    lo |= (uint32_t)(q & 0xFF) << (8 * j);
+                    lo = __builtin_amdgcn_cvt_pk_u8_f32(q, j, lo);
                 else
-                    hi |= (uint32_t)(q & 0xFF) << (8 * (j - 4));
+                    hi = __builtin_amdgcn_cvt_pk_u8_f32(q, j - 4, hi);
             }
-            *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo, hi};
+            *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
         }
     }
     if (t == 0) sx[row] = s;

@@ -90,6 +90,36 @@ def test_per_token_edge_rows():
     assert_same_bits(host(sx), s_ref, "sx")
 
 
+def test_per_token_quotients_next_to_rounding_ties():
+    """Smoothed activations X' placed within 0..3 fp32 ulps of (m + 1/2) s,
+    with s = max|X'| / 127 of the token, so X' / s lands next to (or on) a
+    half-way point: the codes decide between two integers there, and the
+    division must be the IEEE one for them to agree bit for bit. Token i is
+    token 0 times 2^(i - 2) (exact in bf16), so every token carries the same
+    near-tie quotients at its own magnitude."""
+    t, k = 6, 1024
+    rng = np.random.default_rng(31)
+    x0 = f32_to_bf16_bits(rng.uniform(1.0, 2.0, k)).astype(np.uint32) << 16
+    x0 = x0.view(np.float32)
+    xs = f32_to_bf16_bits(np.stack([x0 * np.float32(2.0 ** (i - 2)) for i in range(t)]))
+    s0 = rng.uniform(0.5, 2.0)
+    target = np.empty(k)
+    target[0] = 127.0 * s0
+    target[1:] = (rng.integers(-126, 126, k - 1) + 0.5) * s0
+    ulps = rng.integers(-3, 4, k)
+    ulps[0] = 0
+    t32 = target.astype(np.float32)
+    for j in range(1, k):
+        for _ in range(abs(int(ulps[j]))):
+            t32[j] = np.nextafter(t32[j], np.float32(np.inf if ulps[j] > 0 else -np.inf), dtype=np.float32)
+    sm = (x0.astype(np.float64) / t32.astype(np.float64)).astype(np.float32)
+    say("quant_per_token_int8 near-tie quotients")
+    qx, sx = bg.quant_per_token_int8(dev_bf16(xs), dev(sm))
+    q_ref, s_ref = oracle.quant_per_token_int8(xs, sm)
+    assert_same_bits(host(sx), s_ref, "sx")
+    assert_same_bits(host(qx), q_ref, "qx")
+
+
 def test_smoothed_weight_quantization_chain():
     """s from the GPU, then W * s per-channel INT8 on both sides."""
     x, w = _xw(128, 256, 4096, seed=11)
