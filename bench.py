@@ -41,7 +41,7 @@ INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, published
 # compiles out): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
 FP32_FMA_TFLOPS = 78.6
 DOMINANT_SRC = os.path.join(ROOT, "bit_gemv_amd", "csrc", "gemv.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "gemv_w4a16_llama70b_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
 def log(*a):
@@ -617,6 +617,8 @@ def measure_c1_c2(dev) -> dict:
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_kt -o kt -- "
              "python3 $REPO/bench.py --steps 5 --warmup 2 --skip-cpu")
 PMC_CMD = "rocprofv3 --pmc {c} -d $REPO/gpurun_out/prof_{d} -o {d} -- python3 $REPO/bench.py --counter-pass"
+UTIL_CMD = PMC_CMD.format(c="MfmaUtil VALUBusy SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_I8 "
+                            "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE", d="util")
 
 
 def _kernel_short_name(name: str) -> str:
@@ -634,8 +636,10 @@ def _kernel_short_name(name: str) -> str:
     return name
 
 
-def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
-    """Write profiles/*.md and the counter JSON from three rocprofv3 databases."""
+def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, util_db: str = "") -> int:
+    """Write profiles/*.md and the counter JSON from the rocprofv3 databases
+    (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass, and optionally the pass
+    with the MFMA / VALU / LDS counters)."""
     import sqlite3
 
     from workloads import WORKLOADS
@@ -665,57 +669,122 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str) -> int:
     with open(os.path.join(ROOT, "profiles", "kernel_trace_llama70b_decode.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
+    # the dominant kernel's trace average, for bench.py's roofline line
+    if dom_avg:
+        n, k = 57344, 8192
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_llama70b_decode.json"), "w") as f:
+            json.dump({"kernel": "lq::gemv_valu_kernel<1, 8, false, true>", "grid": 7168 * 256,
+                       "dominant_avg_us": round(dom_avg, 3),
+                       "dominant_bytes": w4_bytes(n, k, 1, wl.symmetric, wl.group),
+                       "kernel_source_sha256_16": kernel_source_hash(), "command": TRACE_CMD}, f, indent=1)
+            f.write("\n")
+
     # counters: calibrate FETCH_SIZE / WRITE_SIZE (KiB) on the 1 GiB copy
     def counter(db, cname):
         cc = sqlite3.connect(db)
-        recs = cc.execute("select kernel_name, grid_size, value from counters_collection where counter_name = ? "
+        return cc.execute("select kernel_name, grid_size, value from counters_collection where counter_name = ? "
                           "order by dispatch_id", (cname,)).fetchall()
-        # the three 1 GiB copies: the largest copyBuffer dispatches
-        copy = sorted((v for nm, g, v in recs if "copyBuffer" in nm), reverse=True)[:3]
-        gemv = [v for nm, g, v in recs if "gemv_valu_kernel" in nm]
-        return copy, gemv
 
-    fcopy, fgemv = counter(fetch_db, "FETCH_SIZE")
-    wcopy, wgemv = counter(write_db, "WRITE_SIZE")
+    frecs, wrecs = counter(fetch_db, "FETCH_SIZE"), counter(write_db, "WRITE_SIZE")
+    fcopy = sorted((v for nm, g, v in frecs if "copyBuffer" in nm), reverse=True)[:3]
+    wcopy = sorted((v for nm, g, v in wrecs if "copyBuffer" in nm), reverse=True)[:3]
     gib_kib = float(1 << 20)
     ffac = (sum(fcopy) / len(fcopy)) / gib_kib
     wfac = (sum(wcopy) / len(wcopy)) / gib_kib
-    f_kib = sum(fgemv) / len(fgemv)
-    w_kib = sum(wgemv) / len(wgemv)
-    n, k = 57344, 8192
-    alg = w4_bytes(n, k, 1, wl.symmetric, wl.group)
-    hbm = f_kib * 1024 / ffac + w_kib * 1024 / wfac
+    n, k, M = 57344, 8192, 2048
+    kernels = [
+        ("gemv_valu_kernel", "W4A16 GEMV batch 1, fused gate|up 57344 x 8192 (8 distinct buffers)",
+         w4_bytes(n, k, 1, wl.symmetric, wl.group)),
+        ("quant_team_kernel", "quantize-pack INT4 asym G=128, 57344 x 8192 (the same bf16 W 8 times)",
+         n * k * 2 + n * k // 2 + n * (k // 128) * 8),
+        ("gemm_w4_kernel", "W4A16 prefill GEMM M=2048, 8192 x 8192",
+         M * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 64 * 8 + M * 8192 * 4),
+        ("gemm_mx_kernel", "MXFP4 prefill GEMM M=2048, 8192 x 8192",
+         M * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 256 + M * 8192 * 4),
+        ("w8a8_kernel", "W8A8 GEMM 512 x 8192 x 8192",
+         512 * 8192 + 8192 * 8192 + 512 * 4 + 8192 * 4 + 512 * 8192 * 4),
+    ]
+    per = []
+    for key, what, alg in kernels:
+        fv = [v for nm, g, v in frecs if key in nm]
+        wv = [v for nm, g, v in wrecs if key in nm]
+        if not fv or not wv:
+            continue
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        hbm = f_kib * 1024 / ffac + w_kib * 1024 / wfac
+        per.append({"kernel_match": key, "workload": what, "dispatches": len(fv),
+                    "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+                    "hbm_bytes_per_dispatch": int(round(hbm)), "algorithmic_bytes": alg,
+                    "traffic_over_algorithmic": round(hbm / alg, 4)})
+    gemv = per[0]
     out = {"kernel": "lq::gemv_valu_kernel<1, 8, false, true> (w4a16_gemv, batch 1, asymmetric, staged scales)",
            "workload": "llama70b_decode fused gate|up", "n": n, "k": k,
            "kernel_source_sha256_16": kernel_source_hash(),
-           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "fetch_kib_per_dispatch": gemv["fetch_kib_per_dispatch"],
+           "write_kib_per_dispatch": gemv["write_kib_per_dispatch"],
            "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
                                 "fetch_kib": round(sum(fcopy) / len(fcopy), 1),
                                 "write_kib": round(sum(wcopy) / len(wcopy), 1),
                                 "fetch_factor": round(ffac, 5), "write_factor": round(wfac, 5)},
-           "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes_per_launch": alg,
-           "traffic_over_algorithmic": round(hbm / alg, 4),
+           "hbm_bytes_per_launch": gemv["hbm_bytes_per_dispatch"],
+           "algorithmic_bytes_per_launch": gemv["algorithmic_bytes"],
+           "traffic_over_algorithmic": gemv["traffic_over_algorithmic"],
+           "other_kernels": per[1:],
            "commands": [f"cd /tmp && export TMPDIR=/tmp && {PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
                         f"cd /tmp && export TMPDIR=/tmp && {PMC_CMD.format(c='WRITE_SIZE', d='write')}"]}
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    md = ["# HBM traffic of the batch-1 W4A16 GEMV (fused gate|up, 57344 x 8192)", "",
+    md = ["# HBM traffic of the memory-bound and matrix-core kernels", "",
           "Commands ($REPO = repository root):", "",
           *[f"- `{cmd}`" for cmd in out["commands"]], "",
-          "Each pass runs torch's copy of 1 GiB three times (calibration) and the GEMV once on each of 8 "
-          "address-distinct weight buffers. Counters are per dispatch, in KiB.", "",
-          "| quantity | value |", "|---|---|",
-          f"| copy: FETCH_SIZE for 1 GiB read | {out['copy_calibration']['fetch_kib']} KiB (factor {ffac:.4f}) |",
-          f"| copy: WRITE_SIZE for 1 GiB written | {out['copy_calibration']['write_kib']} KiB (factor {wfac:.4f}) |",
-          f"| GEMV FETCH_SIZE | {out['fetch_kib_per_dispatch']} KiB |",
-          f"| GEMV WRITE_SIZE | {out['write_kib_per_dispatch']} KiB |",
-          f"| GEMV HBM bytes (calibrated) | {out['hbm_bytes_per_launch']} |",
-          f"| GEMV algorithmic bytes | {alg} |",
-          f"| traffic / algorithmic | {out['traffic_over_algorithmic']} |", "",
-          f"Kernel source hash (gemv.hip, sha256, 16 hex): `{out['kernel_source_sha256_16']}`."]
-    with open(os.path.join(ROOT, "profiles", "gemv_w4a16_llama70b_counters.md"), "w") as f:
+          "Each pass runs torch's copy of 1 GiB three times (calibration), the INT4 quantizer 8 times and the "
+          "batch-1 GEMV once on each of 8 address-distinct weight buffers (fused gate|up, 57344 x 8192), then "
+          "the W4A16 and MXFP4 prefill GEMMs (M = 2048, 8192 x 8192) and the W8A8 GEMM (512 x 8192 x 8192) "
+          "twice each. Counters are per dispatch, in KiB, scaled by what they read for the 1 GiB copy.", "",
+          f"Calibration: FETCH_SIZE reads {out['copy_calibration']['fetch_kib']} KiB for 1 GiB read "
+          f"(factor {ffac:.4f}); WRITE_SIZE reads {out['copy_calibration']['write_kib']} KiB for 1 GiB written "
+          f"(factor {wfac:.4f}).", "",
+          "| kernel | workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | "
+          "algorithmic bytes | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for r in per:
+        md.append(f"| `{r['kernel_match']}` | {r['workload']} | {r['dispatches']} | {r['fetch_kib_per_dispatch']} | "
+                  f"{r['write_kib_per_dispatch']} | {r['hbm_bytes_per_dispatch']} | {r['algorithmic_bytes']} | "
+                  f"{r['traffic_over_algorithmic']} |")
+    md += ["", f"Kernel source hash of gemv.hip (sha256, 16 hex): `{out['kernel_source_sha256_16']}`."]
+    with open(os.path.join(ROOT, "profiles", "hbm_counters.md"), "w") as f:
         f.write("\n".join(md) + "\n")
+
+    if util_db:
+        cc = sqlite3.connect(util_db)
+        recs = cc.execute("select kernel_name, counter_name, value from counters_collection "
+                          "order by dispatch_id").fetchall()
+        names = sorted({cn for _, cn, _ in recs})
+        util = []
+        for key, what, _ in kernels:
+            row = {"kernel_match": key, "workload": what}
+            for cn in names:
+                vals = [v for nm, c2, v in recs if key in nm and c2 == cn]
+                if vals:
+                    row[cn] = round(sum(vals) / len(vals), 3)
+            if len(row) > 2:
+                util.append(row)
+        out["utilization"] = util
+        with open(COUNTERS, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        um = ["# Matrix-core, VALU and LDS counters of the same kernels", "",
+              f"Command ($REPO = repository root): `cd /tmp && export TMPDIR=/tmp && {UTIL_CMD}`", "",
+              "Same run as the HBM counters (bench.py --counter-pass); averages per dispatch. MfmaUtil = "
+              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), VALUBusy = SQ_ACTIVE_INST_VALU / (CUs x "
+              "GRBM_GUI_ACTIVE), both in percent; the MOPS counters count MFMA operations in units of 512 "
+              "flops (or int ops).", "",
+              "| kernel | workload | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+        for r in util:
+            um.append(f"| `{r['kernel_match']}` | {r['workload']} | " +
+                      " | ".join(str(r.get(cn, "")) for cn in names) + " |")
+        with open(os.path.join(ROOT, "profiles", "mfma_valu_counters.md"), "w") as f:
+            f.write("\n".join(um) + "\n")
     print(json.dumps(out))
     return 0
 
@@ -731,9 +800,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--skip-rows", action="store_true", help="only the decode sweep")
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
-                    help="turn rocprofv3 databases (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass) into "
-                         "the summaries under profiles/ and exit")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DB",
+                    help="turn rocprofv3 databases (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass and optionally "
+                         "the MFMA/VALU/LDS pass) into the summaries under profiles/ and exit")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: a 1 GiB copy (counter calibration), then the "
                          "dominant GEMV once on each of 8 address-distinct layers")
@@ -766,7 +835,32 @@ def counter_pass() -> int:
     for p in packs:
         bg.w4a16_gemv(x, p, y)
     torch.cuda.synchronize()
-    log(f"[bench] counter pass done: copy 1 GiB x3, gemv {packs[0].n}x{packs[0].k} x{len(packs)}")
+    del packs, x, y
+    torch.cuda.empty_cache()
+    # the matrix-core kernels, twice each: W4A16 and MXFP4 prefill GEMM at
+    # M = 2048 on the 8192 x 8192 layer, and the W8A8 GEMM of the SmoothQuant
+    # workload (512 x 8192 x 8192)
+    pf = WORKLOADS["prefill70b"]
+    w = torch.from_numpy(pf.weight(0, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+    xg = torch.from_numpy(pf.activation(8192, pf.tokens).view(np.int16)).view(torch.bfloat16).to(dev)
+    pw = bg.quantize_groupwise(w, 4, pf.symmetric, pf.group)
+    mw = bg.mxfp4_quantize(w)
+    yg = torch.empty((pf.tokens, 8192), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        bg.w4a16_gemm(xg, pw, yg)
+    for _ in range(2):
+        bg.mxfp4_gemm(xg, mw, yg)
+    sq = WORKLOADS["smoothquant"]
+    xs = torch.from_numpy(sq.activation(8192, sq.tokens).view(np.int16)).view(torch.bfloat16).to(dev)
+    s = bg.smooth_scale(xs, w, sq.extra["alpha"])
+    qw = bg.quantize_groupwise(w, 8, True, 8192, s)
+    qx, sx = bg.quant_per_token_int8(xs, s)
+    y8 = torch.empty((sq.tokens, 8192), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        bg.w8a8_gemm(qx, sx, qw.codes.view(torch.int8), qw.scales.view(-1), y=y8)
+    torch.cuda.synchronize()
+    log("[bench] counter pass done: copy 1 GiB x3, quantize 57344x8192 x8, gemv x8, gemm/mxfp4_gemm M=2048 x2, "
+        "w8a8 512x8192x8192 x2")
     return 0
 
 
