@@ -19,10 +19,18 @@
 //  * a stage is 256 k of INT4 or MXFP4 codes or 128 k of INT8 codes: 128
 //    bytes of every row either way, 16 KB per block;
 //  * per stage every wave issues 4 of the block's 16 code loads (8 rows x
-//    128 bytes each), its share of the XR activation rows (XR = the batch
-//    rounded up to 4, 8 or 16; rows past the batch read zeros) and a quarter
-//    of the stage's scales (and zeros), all as buffer loads in the LDS-write
-//    form, so no operand passes through registers on its way to LDS;
+//    128 bytes each) and its share of the XR activation rows (XR = the batch
+//    rounded up to 4, 8 or 16; rows past the batch read zeros), all as buffer
+//    loads in the LDS-write form, so no operand passes through registers on
+//    its way to LDS;
+//  * scales and zeros come in windows of kWinSt (4, or 2 for INT4 at XR =
+//    16) stages, double-buffered: at a window's first stage each wave loads
+//    its quarter of the window, 4 bytes a lane with the lanes of a row
+//    reading its consecutive entries (8 or 16 rows of 16-32 bytes per load).
+//    Loading each stage's entries for the 128 rows instead costs a separate
+//    cache line per lane; on the 70B shapes the windows take 10-16 % off
+//    INT8 at batch 8-16, 2-21 % off MXFP4 and 5-14 % off INT4 on q|k|v,
+//    gate|up and o at batch 4 (within a few per cent either way elsewhere);
 //  * three slots: one stage is computed while the next is in flight. The
 //    stage wait is the wave's own vmcnt (loads that write LDS are only
 //    counted there) followed by a barrier; the slot refilled after it is the
@@ -47,9 +55,12 @@
 // LDS layout of a slot: codes [128 rows][128 B], 16-byte chunk c of row r
 // stored at c ^ ((r >> 1) & 7); activations [XR rows][2 x stage k bytes],
 // chunk c of row r at c ^ r (batch column b reads row b % XR; columns past
-// the batch are never stored); then the scales of the stage. With these the
-// 16 rows (columns) of one fragment read fall in distinct banks. At most
-// 79,872 bytes, so 2 blocks fit a CU.
+// the batch are never stored). With these the 16 rows (columns) of one
+// fragment read fall in distinct banks. The two window buffers follow the
+// three slots in the same array: with the windows declared as an array of
+// their own, the compiler made every wave wait for all of its outstanding
+// LDS-write loads before each window read, which stalled the ring. At most
+// 81,920 bytes, so 2 blocks fit a CU.
 // With too few row blocks to fill the chip, k is split into runs of stages
 // (blockIdx.y); the runs add their partial sums into y, zeroed first on the
 // same stream, with float atomics, so with more than two runs the summation
@@ -76,7 +87,7 @@ struct ShFormat {
     static constexpr int kXRowBytes = 2 * kStageK;                        // activation bytes a row per stage
     static constexpr int kXChunks = kXRowBytes / 16;
     static constexpr int kXRowsPerPiece = 1024 / kXRowBytes;              // rows in a 1 KB load
-    static constexpr int kMetaBytes = F == WeightFormat::kInt4 ? 2048 : 1024;
+    static constexpr int kMetaPerStage = F == WeightFormat::kInt8 ? 4 : 8;  // metadata bytes a row per stage
 };
 
 // Four code bytes u0..u3 -> bf16 pairs (u0, u1), (u2, u3): the byte-wise
@@ -106,13 +117,24 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
     constexpr bool kInt4 = F == WeightFormat::kInt4, kInt8 = F == WeightFormat::kInt8, kMx = F == WeightFormat::kMx;
     constexpr int kXPieces = XR * Fm::kXRowBytes / 1024;                  // 1 KB activation loads per stage
     constexpr int kXPerWave = kXPieces >= 4 ? kXPieces / 4 : 1;
-    constexpr int kXOff = kShRows * 128, kSOff = kXOff + XR * Fm::kXRowBytes, kDummy = kSOff + Fm::kMetaBytes;
+    constexpr int kXOff = kShRows * 128, kDummy = kXOff + XR * Fm::kXRowBytes;
     constexpr int kSlot = kDummy + (kXPieces < 4 * kXPerWave ? 1024 : 0);  // a sink for waves without a piece
-    constexpr int kMetaLoads = kInt4 && !SYM ? 2 : 1;
-    constexpr int kVm = (kShSlots - 2) * (4 + kXPerWave + kMetaLoads);  // loads younger than the awaited stage
-    static_assert(kXPerWave <= 2 && kShSlots * kSlot <= 80 * 1024 && XR * (kShRows + 1) * 4 <= kShSlots * kSlot,
-                  "slot layout");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kShSlots * kSlot];
+    // metadata windows: kWinSt stages of every row's scales (and zeros), two
+    // buffers after the slots; 4-byte loads, kLpr lanes per row
+    constexpr int kWinSt = kInt4 && XR == 16 ? 2 : 4;
+    constexpr int kWinRow = kWinSt * Fm::kMetaPerStage;  // bytes a row per window and array
+    constexpr int kArrays = kMx || SYM ? 1 : 2;           // scales, zeros
+    constexpr int kWinBuf = kArrays * kShRows * kWinRow;
+    constexpr int kWinOff = kShSlots * kSlot;
+    constexpr int kLpr = kWinRow / 4, kRowsPerPiece = 64 / kLpr, kPiecesPerArr = kShRows / kRowsPerPiece;
+    constexpr int kWinLoads = kArrays * kPiecesPerArr / 4;  // per wave, at a window's first stage
+    constexpr int kVm = (kShSlots - 2) * (4 + kXPerWave);   // loads younger than the awaited stage
+    static_assert(kXPerWave <= 2 && kWinOff + 2 * kWinBuf <= 80 * 1024 && XR * (kShRows + 1) * 4 <= kWinOff &&
+                      kArrays * kPiecesPerArr % 4 == 0 && kWinSt >= kShSlots - 1,
+                  "slot and window layout");
+    // one array for slots and windows: the compiler makes a wave wait for all
+    // of its LDS-write loads before reading a separately declared array
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kWinOff + 2 * kWinBuf];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, kq = lane >> 4;
@@ -123,14 +145,14 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
     const int s1 = min(nst, s0 + stages_per_run);
     const int rows_here = min(kShRows, n - row0);
     // per-row metadata entries: groups (INT4, INT8) or scale bytes (MXFP4)
-    const int meta_row = kMx ? k / 32 : k / group;
-    const int meta_size = kMx ? 1 : 4;
     // rows past n, k past the row and batch rows past bsz read zeros
     const auto rc = make_rsrc(codes + (int64_t)row0 * row_bytes, (uint32_t)rows_here * row_bytes);
     const auto rx = make_rsrc(x, (uint32_t)bsz * (uint32_t)k * 2);
-    const auto rs = make_rsrc(static_cast<const uint8_t *>(scales) + (int64_t)row0 * meta_row * meta_size,
+    const int64_t meta_row = kMx ? k / 32 : k / group;  // entries a row
+    const int meta_size = kMx ? 1 : 4;
+    const auto rs = make_rsrc(static_cast<const uint8_t *>(scales) + row0 * meta_row * meta_size,
                               (uint32_t)(rows_here * meta_row * meta_size));
-    const auto rz = make_rsrc(kMx || SYM ? static_cast<const float *>(nullptr) : zeros + (int64_t)row0 * meta_row,
+    const auto rz = make_rsrc(kMx || SYM ? static_cast<const float *>(nullptr) : zeros + row0 * meta_row,
                               kMx || SYM ? 0u : (uint32_t)(rows_here * meta_row) * 4);
 
     // code piece p = 4 wave + i: rows 8 p + lane / 8, stored chunk lane % 8
@@ -153,14 +175,21 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
         x_real[i] = q < kXPieces;
         x_off[i] = (uint32_t)xr * (uint32_t)k * 2 + 16u * (uint32_t)((lane % Fm::kXChunks) ^ xr);
     }
-    // metadata entry e = 64 wave + lane, 4 bytes each, stored at 4 e:
-    //  INT4: half e / 128 of the stage, row e % 128 (scales; zeros 1 KB on);
-    //  INT8: scale (e < 128) or zero (e >= 128) of row e % 128;
-    //  MXFP4: scale bytes 4 (e % 2) .. + 3 of the stage of row e / 2.
-    const int se = 64 * wave + lane;
-    const int m_row = kMx ? se >> 1 : se & (kShRows - 1);
-    const int m_half = kInt4 ? se >> 7 : kMx ? se & 1 : 0;
-    const bool m_zero = kInt8 && wave >= 2;  // wave-uniform
+    // A window holds, per row and array, one fp32 entry per 128-wide
+    // half-stage (INT4, INT8: the scale or zero of the group the half lies
+    // in; kLpr entries) or the E8M0 bytes of its stages (MXFP4, 8 a stage).
+    // Layout of an array: INT4, INT8 [row / 4][entry][row % 4] (fp32), so the
+    // four rows a lane's accumulators hold are one 16-byte read; MXFP4
+    // [row][byte]. A 4-byte window load (piece p = kWinLoads wave + i, array
+    // p / kPiecesPerArr, kRowsPerPiece rows) covers 256 contiguous LDS bytes;
+    // lane l holds row rbase + 4 (l / (4 kLpr)) + l % 4, entry (l / 4) % kLpr
+    // (INT4, INT8), or row rbase + l / kLpr, bytes 4 (l % kLpr) .. + 3 (MXFP4).
+    const uint32_t meta_row_bytes = (uint32_t)((kMx ? k / 32 : k / group) * (kMx ? 1 : 4));
+    const int w_row = kMx ? lane / kLpr : 4 * (lane / (4 * kLpr)) + lane % 4;  // row within the piece
+    const int w_ent = kMx ? lane % kLpr : (lane / 4) % kLpr;                    // word within the row
+    auto win_word = [&](int ws) -> uint32_t {  // this lane's byte in its row, window from stage ws
+        return kMx ? (uint32_t)(ws * 8 + 4 * w_ent) : (uint32_t)(((ws * kStageK + 128 * w_ent) / group) * 4);
+    };
 
     auto issue = [&](int st) {
         uint8_t *slot = ring + (st % kShSlots) * kSlot;
@@ -177,20 +206,20 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
                 (__attribute__((address_space(3))) void *)(slot + (x_real[i] ? kXOff + 1024 * (kXPerWave * wave + i)
                                                                              : kDummy)),
                 16, in && x_real[i] ? x_off[i] + (uint32_t)st * kXRowBytes : kOutOfRange, 0, 0, 0);
-        const int kk = st * kStageK + 128 * m_half;  // first k the entry covers
-        const bool m_in = in && kk < k && m_row < rows_here;
-        uint32_t mo;
-        if constexpr (kMx)
-            mo = (uint32_t)(m_row * meta_row + st * 8 + 4 * m_half);
-        else
-            mo = (uint32_t)(m_row * meta_row + kk / group) * 4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_zero ? rz : rs,
-                                                 (__attribute__((address_space(3))) void *)(slot + kSOff + 256 * wave),
-                                                 4, m_in ? mo : kOutOfRange, 0, 0, 0);
-        if constexpr (kMetaLoads == 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rz, (__attribute__((address_space(3))) void *)(slot + kSOff + 1024 + 256 * wave), 4,
-                m_in ? mo : kOutOfRange, 0, 0, 0);
+        if ((st - s0) % kWinSt == 0) {  // a window's first stage (wave-uniform)
+            uint8_t *win = ring + kWinOff + (((st - s0) / kWinSt) & 1) * kWinBuf;
+            const uint32_t word = win_word(st);
+#pragma unroll
+            for (int i = 0; i < kWinLoads; ++i) {
+                const int p = kWinLoads * wave + i;
+                const int arr = p / kPiecesPerArr, rbase = kRowsPerPiece * (p % kPiecesPerArr);
+                const int r = rbase + w_row;
+                const uint32_t off = (uint32_t)r * meta_row_bytes + word;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    arr ? rz : rs, (__attribute__((address_space(3))) void *)(win + arr * kShRows * kWinRow + rbase * kWinRow),
+                    4, in && r < rows_here ? off : kOutOfRange, 0, 0, 0);
+            }
+        }
     };
 
     uint32_t magic;
@@ -224,12 +253,21 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
     for (int st = s0; st < s1; ++st) {
         // stage st has landed for every wave; the slot refilled below was
         // last read in the previous iteration, before this barrier
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+        // (stage st + 1 carries a window's loads when it starts one)
+        if ((st + 1 - s0) % kWinSt == 0)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm + kWinLoads) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
         issue(st + kShSlots - 1);
         const uint8_t *slot = ring + (st % kShSlots) * kSlot;
-        const float *sz = reinterpret_cast<const float *>(slot + kSOff);
+        const int ws = st - (st - s0) % kWinSt;  // first stage of the window
+        const uint8_t *win = ring + kWinOff + (((st - s0) / kWinSt) & 1) * kWinBuf;
 #pragma unroll
         for (int h = 0; h < Fm::kHalves; ++h) {
+            // a half past the row's end (k a multiple of 128 only) is skipped:
+            // its code and activation reads run into the next rows and its
+            // window entries are the next row's
+            if (st * kStageK + 128 * h >= k) break;
             bf16x8_t bop[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bop[j] = *reinterpret_cast<const bf16x8_t *>(slot + b_off[h][j]);
@@ -260,7 +298,7 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
                         for (int j = 0; j < 4; ++j) aop[j] = __builtin_bit_cast(bf16x8_t, unpack_natural(w[j], magic));
                     } else {
                         // the lane's chunk is block 4 h + lane / 16 of the stage
-                        const uint32_t e8 = slot[kSOff + 8 * (32 * wave + 16 * t + l16) + 4 * h + kq];
+                        const uint32_t e8 = win[kWinRow * (32 * wave + 16 * t + l16) + 8 * (st - ws) + 4 * h + kq];
                         const float scale = __uint_as_float(e8 << 23);  // 2^(e8 - 127); the byte 0 acts as 2^-127
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -282,11 +320,11 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
                     for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[j], bop[j], d, 0, 0, 0);
                     // D rows 4 (lane / 16) + v of the tile
                     const int rb = 32 * wave + 16 * t + 4 * kq;
-                    const int sb = kInt4 ? h * kShRows + rb : rb;
-                    const int zb = kInt4 ? 2 * kShRows + sb : kShRows + rb;
-                    const f32x4 sv = *reinterpret_cast<const f32x4 *>(&sz[sb]);
+                    // the half-stage's entries of rows rb .. rb + 3 in the window
+                    const int eo = ((rb / 4) * kLpr + Fm::kHalves * (st - ws) + h) * 16;
+                    const f32x4 sv = *reinterpret_cast<const f32x4 *>(win + eo);
                     f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if constexpr (!SYM) zv = *reinterpret_cast<const f32x4 *>(&sz[zb]);
+                    if constexpr (!SYM) zv = *reinterpret_cast<const f32x4 *>(win + kShRows * kWinRow + eo);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const float c = kInt4 ? (SYM ? 136.0f : 128.0f + zv[v]) : (SYM ? 128.0f : zv[v]);
