@@ -87,8 +87,10 @@ __global__ __launch_bounds__(512) void gemm_w4_kernel(const uint16_t *__restrict
                                                        const float *__restrict__ scales,
                                                        const float *__restrict__ zeros, int group,
                                                        float *__restrict__ y, GemmBatch batch) {
+    // the only LDS array (with a second one declared, the compiler waits for
+    // all of a wave's LDS-write loads before every fragment read); the loss
+    // epilogue reuses its first bytes
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kSlot];
-    __shared__ double wave_loss[kWaves];
     x += (int64_t)blockIdx.y * batch.x_stride;
     codes += (int64_t)blockIdx.y * batch.code_stride;
     scales += (int64_t)blockIdx.y * batch.meta_stride;
@@ -278,6 +280,10 @@ __global__ __launch_bounds__(512) void gemm_w4_kernel(const uint16_t *__restrict
                 }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+        // every wave's trailing loads have landed (each waited for its own
+        // above) and no wave reads the ring any more past this barrier
+        __syncthreads();
+        double *wave_loss = reinterpret_cast<double *>(&ring[0][0]);
         if (lane == 0) wave_loss[wave] = sq;
         __syncthreads();
         if (tid == 0)

@@ -426,8 +426,12 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
                   "ring vmcnt");
     // one fixed-size array (a lambda capturing an array whose size depends on
     // a template parameter is dropped from the host compilation)
+    // the only LDS array: with a second one declared the compiler waits for
+    // all of a wave's LDS-write loads before every fragment read
     __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kRingWaveBytes];
-    __shared__ float red[4][16][17];
+    // after the loop each wave's partial sums [16][17] go to the start of its
+    // own ring region
+    auto red = [&](int w) { return reinterpret_cast<float (*)[17]>(ring + w * kRingWaveBytes); };
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, kq = lane >> 4;
@@ -555,11 +559,11 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     // builtin also tells the compiler nothing is pending
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 layout)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * kq + v][l16] = acc[v];
+    for (int v = 0; v < 4; ++v) red(wave)[4 * kq + v][l16] = acc[v];
     __syncthreads();
     {
         const int rr = threadIdx.x >> 4, col = threadIdx.x & 15;
-        const float v = red[0][rr][col] + red[1][rr][col] + red[2][rr][col] + red[3][rr][col];
+        const float v = red(0)[rr][col] + red(1)[rr][col] + red(2)[rr][col] + red(3)[rr][col];
         const int row = row0 + rr;
         if (row < n && col < bsz) y[(int64_t)col * n + row] = v;
     }
@@ -582,14 +586,18 @@ static hipError_t launch_valu_rw(const WoArgs &a, hipStream_t st, int ks_count) 
 
 // Launch shape (measured on MI355X): the block's four waves split k four
 // ways when a row has 4..7 chunks, two ways when it has 2..3 or 8 and more
-// (then each wave walks several chunks), not at all for one chunk; a wave
-// takes 8 rows unless that leaves fewer than 512 blocks to fill the chip.
+// (then each wave walks several chunks), not at all for one chunk. A wave
+// takes 8 rows, except where 4 rows measured faster: with one chunk, below
+// 512 blocks of 8 rows; with the four-way split, at up to 512 blocks
+// (4096 x 11008: 7.7 against 8.3 us). With the two-way split 8 rows win
+// also on 256 blocks (4096 x 4096: 4.2 against 4.4 us).
 template <int B, bool SYM>
 static hipError_t launch_valu(const WoArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
     const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
     const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
-    return blocks8 >= 512 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
+    const bool rw8 = ks == 2 ? true : ks == 4 ? blocks8 > 512 : blocks8 >= 512;
+    return rw8 ? launch_valu_rw<B, 8, SYM>(a, st, ks) : launch_valu_rw<B, 4, SYM>(a, st, ks);
 }
 
 // Waves per block: enough to put about 2048 waves on the chip (8 per CU),
