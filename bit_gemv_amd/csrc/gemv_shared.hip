@@ -423,8 +423,10 @@ hipError_t launch_fmt(const SharedGemvArgs &a, hipStream_t st) {
 
 // Where the shared-stage kernel beats the other kernels of its format
 // (measured on MI355X over the 7B and 70B linears and ragged shapes):
-//  INT4: batch 4..16 from about 40M weights (1.0-2.1x; below that the
-//        LDS-ring kernel is faster);
+//  INT4: batch 5..16 from about 40M weights (1.0-2.1x; below that the
+//        LDS-ring kernel is faster), batch 4 from 40M weights where k >
+//        8192 and from 64Mi weights otherwise (the VALU kernel: 8-19 %
+//        faster on 6144 x 8192 and 12288 x 4096);
 //  INT8: batch 5..8 from 40M weights, 9..16 from 16M (1.1-2.9x); at batch 4
 //        the VALU kernel wins or ties;
 //  MXFP4: batch 4..8 from 40M weights, 9..16 from 16M (1.1-4.9x).
@@ -437,7 +439,9 @@ bool shared_gemv_pays(WeightFormat f, int64_t m, int64_t n, int64_t k) {
     const int64_t weights = n * k;
     const bool large = weights >= (int64_t(40) << 20), medium = weights >= (int64_t(16) << 20);
     switch (f) {
-        case WeightFormat::kInt4: return large;
+        // at batch 4 the VALU kernel stays ahead up to 64Mi weights with
+        // k <= 8192 (12288 x 4096 symmetric: 10.2 against 12.5 us)
+        case WeightFormat::kInt4: return m == 4 ? large && (k > 8192 || weights >= (int64_t(64) << 20)) : large;
         case WeightFormat::kInt8: return m >= 9 ? medium : m >= 5 && large;
         case WeightFormat::kMx: return m >= 9 ? medium : large;
     }
