@@ -228,7 +228,7 @@ static hipError_t launch8_s(const WoArgs &a, hipStream_t st) {
 
 hipError_t launch_w8a16_gemv(const WoArgs &a, hipStream_t st) {
     if (a.m < 1 || a.m > 16) return hipErrorInvalidValue;
-    // batch 5..16 on large matrices: the shared-stage kernel of gemv_shared.hip
+    // batch 4..16 on large matrices: the shared-stage kernel of gemv_shared.hip
     if (shared_gemv_pays(WeightFormat::kInt8, a.m, a.n, a.k)) {
         const SharedGemvArgs sa{a.x, a.m, a.codes, a.scales, a.zeros, a.n, a.k, a.symmetric, a.group, a.y};
         return launch_shared_gemv(WeightFormat::kInt8, sa, st);

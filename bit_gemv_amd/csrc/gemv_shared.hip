@@ -427,8 +427,8 @@ hipError_t launch_fmt(const SharedGemvArgs &a, hipStream_t st) {
 //        LDS-ring kernel is faster), batch 4 from 40M weights where k >
 //        8192 and from 64Mi weights otherwise (the VALU kernel: 8-19 %
 //        faster on 6144 x 8192 and 12288 x 4096);
-//  INT8: batch 5..8 from 40M weights, 9..16 from 16M (1.1-2.9x); at batch 4
-//        the VALU kernel wins or ties;
+//  INT8: batch 4 from 40M weights with k >= 8192, 5..8 from 40M weights,
+//        9..16 from 16M (1.1-2.9x);
 //  MXFP4: batch 4..8 from 40M weights, 9..16 from 16M (1.1-4.9x).
 // The block's codes (128 rows) and the activations are addressed with
 // 32-bit offsets below 2^31.
@@ -442,7 +442,9 @@ bool shared_gemv_pays(WeightFormat f, int64_t m, int64_t n, int64_t k) {
         // at batch 4 the VALU kernel stays ahead up to 64Mi weights with
         // k <= 8192 (12288 x 4096 symmetric: 10.2 against 12.5 us)
         case WeightFormat::kInt4: return m == 4 ? large && (k > 8192 || weights >= (int64_t(64) << 20)) : large;
-        case WeightFormat::kInt8: return m >= 9 ? medium : m >= 5 && large;
+        // INT8 at batch 4: ahead of the VALU kernel where k >= 8192 (70B
+        // shapes 2-13 %, 4096 x 11008 14 %), behind at k = 4096 (12-17 %)
+        case WeightFormat::kInt8: return m >= 9 ? medium : m >= 5 ? large : large && k >= 8192;
         case WeightFormat::kMx: return m >= 9 ? medium : large;
     }
     return false;
