@@ -89,8 +89,8 @@ def test_extreme_codes():
         assert_close(y, oracle.w8a16_matmul(x, c_ref, s_ref, z_ref, n, k, sym, 128), f"extreme sym={sym}")
 
 
-# Batch 5..8 from about 40M weights and 9..16 from 16M go to the
-# shared-stage kernel: 128-row blocks (ragged here), k in 128-wide stages
+# Batch 4 from about 40M weights with k >= 8192, 5..8 from 40M and 9..16
+# from 16M go to the shared-stage kernel: 128-row blocks (ragged here), k in 128-wide stages
 # split into runs (uneven, some empty) whose partial sums meet in y.
 @pytest.mark.parametrize("b", [5, 8, 9, 16])
 @pytest.mark.parametrize("n,k", [(16384 + 33, 4096 + 384),   # 8 runs of 5 stages, the last empty
@@ -99,6 +99,15 @@ def test_extreme_codes():
                                  (40000 + 77, 2048 + 128)])  # no split
 def test_shared_stage_batches(n, k, b):
     _case(n, k, b, False, seed=n % 83 + b)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(4096 + 17, 11008),       # 16 runs of 6 stages, one with 2, one empty
+                                 (8192 + 100, 8192 + 256)])  # 16 runs of 5, one with 1, two empty
+def test_shared_stage_batch4(n, k, sym):
+    """Batch 4 goes to the shared-stage kernel (4 staged activation rows)
+    from 40M weights where k >= 8192."""
+    _case(n, k, 4, sym, seed=n % 71)
 
 
 @pytest.mark.parametrize("b", [6, 12])
