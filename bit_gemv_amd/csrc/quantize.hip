@@ -166,6 +166,15 @@ LQ_DEVICE float stored_code_fast(float qd, float z) {
     }
 }
 
+// Eight INT4 stored codes (from stored_code_fast) -> one word, element i at
+// bits 4i .. 4i + 3.
+LQ_DEVICE uint32_t pack8_int4(const float c[8]) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * p + 1], 16.0f, c[2 * p]), p, word);
+    return word;
+}
+
 // Stored codes of 8 consecutive elements (from stored_code_fast) -> packed.
 template <int BITS, bool SYM>
 LQ_DEVICE void store8_fast(uint8_t *__restrict__ codes, int64_t elem, const float c[8]) {
@@ -231,6 +240,10 @@ __global__ __launch_bounds__(256) void quant_team_kernel(const uint16_t *__restr
     constexpr int kTeams = 256 / TS;
     constexpr int kChunk = 8 * TS;
     constexpr int G = kChunk * M;
+    // INT4 with 128-element groups on 8-lane teams: a group's 64 code bytes
+    // leave in one store per team (whole lines with the neighbouring team)
+    // instead of two half-filled ones
+    constexpr bool kWholeLines = BITS == 4 && TS == 8 && M == 2;
     const int team = threadIdx.x / TS;
     const int l = threadIdx.x % TS;
     const int64_t g0 = (int64_t)blockIdx.x * (kTeams * GPT) + team;
@@ -269,12 +282,31 @@ __global__ __launch_bounds__(256) void quant_team_kernel(const uint16_t *__restr
         if (fast_group(SYM ? a : fmaxf(-mn, mx))) {
             float y;
             scale_zero_fast<BITS, SYM>(a, mn, mx, s, z, y);
+            if constexpr (kWholeLines) {
+                // the two code words of the lane, then the team's 64 bytes in
+                // one store: lane l takes elements 16 l .. 16 l + 15, i.e. the
+                // words of lanes 2 l and 2 l + 1 of chunk l / 4
+                uint32_t word[2];
 #pragma unroll
-            for (int c = 0; c < M; ++c) {
-                float cf[8];
+                for (int c = 0; c < 2; ++c) {
+                    float cf[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) cf[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][c][j], s, y), z);
-                store8_fast<BITS, SYM>(codes, g * G + kChunk * c + l * 8, cf);
+                    for (int j = 0; j < 8; ++j) cf[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][c][j], s, y), z);
+                    word[c] = pack8_int4(cf);
+                }
+                const int s0 = (2 * l) & 7;
+                const int a0 = __shfl((int)word[0], s0, 8), b0 = __shfl((int)word[1], s0, 8);
+                const int a1 = __shfl((int)word[0], s0 + 1, 8), b1 = __shfl((int)word[1], s0 + 1, 8);
+                const u32x2 v{(uint32_t)(l < 4 ? a0 : b0), (uint32_t)(l < 4 ? a1 : b1)};
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + (g * G) / 2 + 8 * l));
+            } else {
+#pragma unroll
+                for (int c = 0; c < M; ++c) {
+                    float cf[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cf[j] = stored_code_fast<BITS, SYM>(div_rn(x[i][c][j], s, y), z);
+                    store8_fast<BITS, SYM>(codes, g * G + kChunk * c + l * 8, cf);
+                }
             }
         } else {
             scale_zero<BITS, SYM>(a, mn, mx, s, z);
