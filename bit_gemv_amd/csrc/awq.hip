@@ -330,11 +330,13 @@ hipError_t launch_awq_search(const AwqArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(div_act_kernel, dim3(xblocks, (uint32_t)points), dim3(256), 0, st, a.x, x8, (int)a.k, s,
                            s_stride, xa, x_stride);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        for (int p = 0; p < points; ++p) {
-            const QuantArgs q{a.w, a.n, a.k, 4, a.symmetric, a.group, s + p * s_stride, codes + p * code_stride,
-                              scales + p * meta_stride, zeros + p * meta_stride};
-            if ((e = launch_quantize(q, st)) != hipSuccess) return e;
-        }
+        // the batch's quantizations in one launch
+        QuantArgs q{a.w, a.n, a.k, 4, a.symmetric, a.group, s, codes, scales, zeros};
+        q.batch = points;
+        q.cs_stride = s_stride;
+        q.code_stride = code_stride;
+        q.meta_stride = meta_stride;
+        if ((e = launch_quantize(q, st)) != hipSuccess) return e;
         const WoArgs g{xa, a.t, codes, scales, zeros, a.n, a.k, a.symmetric, a.group, nullptr};
         if ((e = launch_w4a16_gemm_loss(g, points, x_stride, code_stride, meta_stride, y_ref, partials, st)) !=
             hipSuccess)

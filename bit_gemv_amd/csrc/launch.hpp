@@ -14,6 +14,11 @@ struct QuantArgs {
     const float *col_scale;
     uint8_t *codes;
     float *scales, *zeros;
+    // batch of products of the same W under different column scales (the AWQ
+    // grid): batch p reads col_scale + p cs_stride and writes codes + p
+    // code_stride (bytes), scales and zeros + p meta_stride (floats)
+    int batch = 1;
+    int64_t cs_stride = 0, code_stride = 0, meta_stride = 0;
 };
 
 struct DequantArgs {

@@ -236,7 +236,13 @@ __global__ __launch_bounds__(256) void quant_team_kernel(const uint16_t *__restr
                                                           const float *__restrict__ cs,
                                                           uint8_t *__restrict__ codes,
                                                           float *__restrict__ scales,
-                                                          float *__restrict__ zeros) {
+                                                          float *__restrict__ zeros, int64_t cs_stride,
+                                                          int64_t code_stride, int64_t meta_stride) {
+    // batch member blockIdx.y (a batch of column scalings of the same W)
+    if (CS) cs += blockIdx.y * cs_stride;
+    codes += blockIdx.y * code_stride;
+    scales += blockIdx.y * meta_stride;
+    if (!SYM) zeros += blockIdx.y * meta_stride;
     constexpr int kTeams = 256 / TS;
     constexpr int kChunk = 8 * TS;
     constexpr int G = kChunk * M;
@@ -604,15 +610,30 @@ template <int BITS, bool SYM, bool CS, int TS, int M, int GPT>
 static hipError_t launch_team(const QuantArgs &a, int64_t ngroups, hipStream_t st) {
     constexpr int64_t per_block = 256 / TS * GPT;
     const int64_t blocks = (ngroups + per_block - 1) / per_block;
-    hipLaunchKernelGGL((quant_team_kernel<BITS, SYM, CS, TS, M, GPT>), dim3((uint32_t)blocks), dim3(256), 0, st,
-                       a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros);
+    hipLaunchKernelGGL((quant_team_kernel<BITS, SYM, CS, TS, M, GPT>), dim3((uint32_t)blocks, (uint32_t)a.batch),
+                       dim3(256), 0, st, a.w, ngroups, a.k, a.col_scale, a.codes, a.scales, a.zeros, a.cs_stride,
+                       a.code_stride, a.meta_stride);
     return hipGetLastError();
 }
 
 template <int BITS, bool SYM, bool CS>
 static hipError_t launch_quant_t(const QuantArgs &a, hipStream_t st) {
     const int64_t ngroups = a.n * (a.k / a.group);
-    if (a.group % 128 == 0 && a.group <= 128 * 8) {
+    const bool team = a.group % 128 == 0 && a.group <= 128 * 8;
+    if (a.batch > 1 && !team) {  // the other kernels take one product per launch
+        for (int p = 0; p < a.batch; ++p) {
+            QuantArgs one = a;
+            one.batch = 1;
+            one.col_scale = a.col_scale ? a.col_scale + p * a.cs_stride : nullptr;
+            one.codes = a.codes + p * a.code_stride;
+            one.scales = a.scales + p * a.meta_stride;
+            one.zeros = a.zeros ? a.zeros + p * a.meta_stride : nullptr;
+            const hipError_t e = launch_quant_t<BITS, SYM, CS>(one, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if (team) {
         switch (a.group / 128) {
             case 1: return launch_team<BITS, SYM, CS, 8, 2, 2>(a, ngroups, st);
             case 2: return launch_team<BITS, SYM, CS, 16, 2, 2>(a, ngroups, st);
