@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restric
     for (int c = 0; c < kMxChunks; ++c) {
         const int64_t i = base + 256 * c;
         // lanes past the end take part in the 4-lane maximum with zeros
-        v[c] = i < total8 ? reinterpret_cast<const u32x4 *>(w)[i] : u32x4{0u, 0u, 0u, 0u};
+        v[c] = i < total8 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w) + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int c = 0; c < kMxChunks; ++c) {
