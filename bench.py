@@ -574,7 +574,14 @@ def measure_c1_c2(dev) -> dict:
     src = []
     for s_ in range(2):
         src.append([torch.cat([dev_bf16(wl.weight(s_, i)) for i in g], 0) for g in groups])
-    packed = [[bg.quantize_groupwise(m, 4, sym, group) for m in src[layer % 2]] for layer in range(wl.layers)]
+    # each matrix in one allocation (codes, scales), so that the read probe
+    # below streams exactly the bytes the GEMV reads
+    flats = [[None] * len(shapes) for _ in range(wl.layers)]
+    packed = [[None] * len(shapes) for _ in range(wl.layers)]
+    for layer in range(wl.layers):
+        for j, m in enumerate(src[layer % 2]):
+            flats[layer][j], packed[layer][j] = flat_packed(dev, shapes[j][0], shapes[j][1], 4, sym, group)
+            bg.quantize_groupwise(m, 4, sym, group, out=packed[layer][j])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -607,8 +614,25 @@ def measure_c1_c2(dev) -> dict:
                           "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4), "bytes": byt}
         log(f"[bench] llama7b_decode batch {b}: {ms:.3f} ms/token, {tbs:.3f} TB/s")
         del xs, ys
+    # the same 128 launches per token of the streaming-read probe over the
+    # same buffers: the rate any one-launch-per-linear design reaches here
+    sink = torch.empty(bg.load_library().lq_read_probe_sink_words(), dtype=torch.int32, device=dev)
+
+    def read_sweep():
+        for layer in range(wl.layers):
+            for j in range(len(shapes)):
+                bg.hbm_read_probe(flats[layer][j], sink)
+
+    rs_ms = _graph_ms(read_sweep, reps=10)
+    read_bytes = wl.layers * sum(f.numel() for f in flats[0])
+    r["hbm_read_ceiling"] = {"kernel": "lq_hbm_read_probe (streaming read, no arithmetic)",
+                             "sweep_TBps": round(read_bytes / (rs_ms * 1e-3) / 1e12, 4),
+                             "sweep_ms_per_token": round(rs_ms, 4), "sweep_bytes": read_bytes,
+                             "batch1_over_probe_rate": round(r["batch1"]["TBps"] / (read_bytes / (rs_ms * 1e-3) / 1e12), 4)}
+    log(f"[bench] llama7b_decode read-probe sweep: {rs_ms:.3f} ms/token, "
+        f"{r['hbm_read_ceiling']['sweep_TBps']:.3f} TB/s")
     rows["llama7b_decode"] = r
-    del packed
+    del packed, flats
     torch.cuda.empty_cache()
     return rows
 
