@@ -686,7 +686,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, util_db: str
         lines.append(f"| `{short}` | {gx} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e6:.3f} |")
     # the fused gate|up launch: 57344 rows / 8 rows per block -> 7168 blocks x 256 work-items
     for name, cnt, avg, mn, mx, tot, gx in rows:
-        if "gemv_valu_kernel<1, 8, false, true>" in name and gx == 7168 * 256:
+        if "gemv_valu_kernel<1, 8, false, true, 4>" in name and gx == 7168 * 256:
             dom_avg = avg / 1e3
     lines += ["", f"Fused gate|up batch-1 GEMV (57344 x 8192, grid {7168 * 256}): average "
                   f"{dom_avg:.2f} us per launch." if dom_avg else ""]
@@ -697,7 +697,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, util_db: str
     if dom_avg:
         n, k = 57344, 8192
         with open(os.path.join(ROOT, "profiles", "kernel_trace_llama70b_decode.json"), "w") as f:
-            json.dump({"kernel": "lq::gemv_valu_kernel<1, 8, false, true>", "grid": 7168 * 256,
+            json.dump({"kernel": "lq::gemv_valu_kernel<1, 8, false, true, 4>", "grid": 7168 * 256,
                        "dominant_avg_us": round(dom_avg, 3),
                        "dominant_bytes": w4_bytes(n, k, 1, wl.symmetric, wl.group),
                        "kernel_source_sha256_16": kernel_source_hash(), "command": TRACE_CMD}, f, indent=1)
@@ -741,7 +741,7 @@ def summarize_profiles(trace_db: str, fetch_db: str, write_db: str, util_db: str
                     "hbm_bytes_per_dispatch": int(round(hbm)), "algorithmic_bytes": alg,
                     "traffic_over_algorithmic": round(hbm / alg, 4)})
     gemv = per[0]
-    out = {"kernel": "lq::gemv_valu_kernel<1, 8, false, true> (w4a16_gemv, batch 1, asymmetric, staged scales)",
+    out = {"kernel": "lq::gemv_valu_kernel<1, 8, false, true, 4> (w4a16_gemv, batch 1, asymmetric, staged scales)",
            "workload": "llama70b_decode fused gate|up", "n": n, "k": k,
            "kernel_source_sha256_16": kernel_source_hash(),
            "fetch_kib_per_dispatch": gemv["fetch_kib_per_dispatch"],

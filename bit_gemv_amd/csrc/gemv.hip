@@ -80,23 +80,24 @@ LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) 
 // 4-byte loads would otherwise be 2 RW of the wave's vector-memory
 // instructions per chunk, and instruction issue, not bytes, bounds the
 // kernel at that point.
-template <int B, int RW, bool SYM, bool G128>
-__global__ __launch_bounds__(256) void gemv_valu_kernel(const uint16_t *__restrict__ x,
-                                                         const uint8_t *__restrict__ codes,
-                                                         const float *__restrict__ scales,
-                                                         const float *__restrict__ zeros, int n, int k,
-                                                         int group, int ks_count, float *__restrict__ y) {
+template <int B, int RW, bool SYM, bool G128, int WPB>
+__global__ __launch_bounds__(WPB * 64) void gemv_valu_kernel(const uint16_t *__restrict__ x,
+                                                              const uint8_t *__restrict__ codes,
+                                                              const float *__restrict__ scales,
+                                                              const float *__restrict__ zeros, int n, int k,
+                                                              int group, int ks_count, float *__restrict__ y) {
     static_assert(!G128 || RW == 4 || RW == 8, "scale staging assumes 4 or 8 rows per wave");
-    __shared__ float red[4][B][RW];
-    __shared__ __attribute__((aligned(16))) float sz_lds[G128 ? 4 : 1][2][16][RW];
+    static_assert(WPB == 4 || WPB == 8, "waves per block");
+    __shared__ float red[WPB][B][RW];
+    __shared__ __attribute__((aligned(16))) float sz_lds[G128 ? WPB : 1][2][16][RW];
     const int lane = threadIdx.x & 63;
     // wave-uniform (scalar) so the buffer resources below live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // ks_count is 1, 2 or 4
-    const int ks_log = ks_count == 4 ? 2 : ks_count - 1;
+    // ks_count is a power of two up to WPB
+    const int ks_log = __builtin_ctz((unsigned)ks_count);
     const int ks = wave & (ks_count - 1);
     const int rs = wave >> ks_log;
-    const int row0 = (blockIdx.x * (4 >> ks_log) + rs) * RW;
+    const int row0 = (blockIdx.x * (WPB >> ks_log) + rs) * RW;
     const int ng = k / group;
     const int nchunks = (k + kChunk - 1) / kChunk;
     const uint32_t row_bytes = (uint32_t)k / 2;
@@ -569,18 +570,18 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint16_t *__restri
     }
 }
 
-template <int B, int RW, bool SYM>
+template <int B, int RW, bool SYM, int WPB = 4>
 static hipError_t launch_valu_rw(const WoArgs &a, hipStream_t st, int ks_count) {
     // staged scales need whole 4-group runs per row: k a multiple of 512
     const bool g128 = a.group == 128 && a.k % 512 == 0;
-    const int rows_per_block = (4 / ks_count) * RW;
+    const int rows_per_block = (WPB / ks_count) * RW;
     const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
     if (g128)
-        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, true>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x,
-                           a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, true, WPB>), dim3((uint32_t)blocks), dim3(WPB * 64), 0, st,
+                           a.x, a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
     else
-        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, false>), dim3((uint32_t)blocks), dim3(256), 0, st, a.x,
-                           a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
+        hipLaunchKernelGGL((gemv_valu_kernel<B, RW, SYM, false, WPB>), dim3((uint32_t)blocks), dim3(WPB * 64), 0,
+                           st, a.x, a.codes, a.scales, a.zeros, (int)a.n, (int)a.k, (int)a.group, ks_count, a.y);
     return hipGetLastError();
 }
 
@@ -590,10 +591,14 @@ static hipError_t launch_valu_rw(const WoArgs &a, hipStream_t st, int ks_count) 
 // takes 8 rows, except where 4 rows measured faster: with one chunk, below
 // 512 blocks of 8 rows; with the four-way split, at up to 512 blocks
 // (4096 x 11008: 7.7 against 8.3 us). With the two-way split 8 rows win
-// also on 256 blocks (4096 x 4096: 4.2 against 4.4 us).
+// also on 256 blocks (4096 x 4096: 4.2 against 4.4 us). At batch 1 with 5..7
+// chunks, blocks of 8 waves split k eight ways, so that no wave walks a
+// second chunk after its first (4 rows a wave; 4096 x 11008: 7.0 against
+// 7.85 us; with 4 or 8 chunks, and 14, the four-wave shapes are as fast).
 template <int B, bool SYM>
 static hipError_t launch_valu(const WoArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk - 1) / kChunk);
+    if (B == 1 && nchunks >= 5 && nchunks <= 7) return launch_valu_rw<B, 4, SYM, 8>(a, st, 8);
     const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
     const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
     const bool rw8 = ks == 2 ? true : ks == 4 ? blocks8 > 512 : blocks8 >= 512;

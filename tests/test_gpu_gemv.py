@@ -28,7 +28,7 @@ def _case(n, k, b, sym, group=128, seed=0, w_scale=0.02, x_mult=None):
 
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("n,k", [(1, 128), (5, 384), (67, 2048 + 128), (300, 4096), (129, 11008),
-                                 (96, 8192), (33, 28672)])
+                                 (96, 8192), (33, 28672), (40, 9728), (61, 10368), (1001, 14336)])
 def test_batch1_shapes(n, k, sym):
     _case(n, k, 1, sym)
 
@@ -106,6 +106,13 @@ def test_mfma_larger_groups(b, group):
 def test_larger_groups(group):
     k = 2048
     _case(77, k, 3, False, group=k if group == "k" else group)
+
+
+@pytest.mark.parametrize("group", [256, "k"])
+def test_larger_groups_eight_way_split(group):
+    # batch 1 with 5..7 chunks of 2048 runs on 8-wave blocks
+    k = 11008 if group == 256 else 12288
+    _case(77, k, 1, True, group=k if group == "k" else group)
 
 
 def test_activation_outlier_channels():
