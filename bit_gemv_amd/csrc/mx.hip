@@ -243,14 +243,16 @@ hipError_t launch_mx_rw(const MxArgs &a, hipStream_t st, int ks_count) {
 
 // Launch shape as the INT4 kernel (same code bytes per chunk): k split 4
 // ways at 4..7 chunks a row, 2 ways at 2..3 or 8 and more; 8 rows a wave
-// (batch up to 4) while that leaves 512 blocks.
+// (batch up to 4) from 512 blocks, with the four-way split from more than
+// 512 (measured at batch 1: the 70B shapes are at the best of ks x rows;
+// 4096 x 11008 takes 7.35 us with 4 rows against 8.12 with 8).
 template <int B>
 hipError_t launch_mx(const MxArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kMxChunk - 1) / kMxChunk);
     const int ks = nchunks >= 8 ? 2 : nchunks >= 4 ? 4 : nchunks >= 2 ? 2 : 1;
     const int64_t blocks8 = (a.n + (4 / ks) * 8 - 1) / ((4 / ks) * 8);
     if constexpr (B <= 4) {  // 8 rows at larger batches would not fit the registers
-        if (blocks8 >= 512) return launch_mx_rw<B, 8>(a, st, ks);
+        if (ks == 4 ? blocks8 > 512 : blocks8 >= 512) return launch_mx_rw<B, 8>(a, st, ks);
     }
     return launch_mx_rw<B, 4>(a, st, ks);
 }

@@ -71,7 +71,7 @@ def _gemv_case(n, k, b, seed, what=""):
 
 
 @pytest.mark.parametrize("n,k", [(1, 128), (5, 384), (67, 2048 + 128), (300, 4096), (129, 11008), (33, 28672),
-                                 (16384 + 37, 2048 + 512), (8192 + 3, 16384 + 512)])
+                                 (16384 + 37, 2048 + 512), (8192 + 3, 16384 + 512), (4096, 9216)])
 def test_gemv_batch1(n, k):
     """One to many chunks of 2048 k, partial last chunks, ragged rows, and
     tall matrices (8 rows per wave)."""
