@@ -64,8 +64,9 @@ LQ_DEVICE float dot8(uint32_t w, const uint32_t *xp, float acc, uint32_t magic) 
 
 // ---------------------------------------------------------------------------
 // VALU kernel, batch B <= 4.
-// Block = 4 waves. The waves split the 2048-wide chunks of k (ks_count ways)
-// and the block's rows (4 / ks_count row sets of RW rows). For each chunk a
+// Block = WPB waves (4, or 8 for an eight-way k split). The waves split the
+// 2048-wide chunks of k (ks_count ways) and the block's rows (WPB / ks_count
+// row sets of RW rows). For each chunk a
 // wave first loads and pairs its 32 activations per batch row (L2 hits),
 // then issues the 16-byte code loads (and scales, zeros) of all RW rows
 // through buffer resources that cover only its rows, so rows past n and
