@@ -8,7 +8,8 @@
  * Memory.   Every tensor pointer is a DEVICE pointer on the current HIP
  *           device, allocated and owned by the caller. The library never
  *           allocates, frees or keeps tensor memory, and keeps no state
- *           between calls except a thread-local error string.
+ *           between calls except a thread-local error string and the one
+ *           static device array of gptq_quantize_noalloc (described there).
  * Layout.   Row-major, the last index contiguous. Weights are W[n][k] with
  *           n = output features and k = input features; activations are
  *           X[m][k]. This is the linear layer Y = X W^T with W[out, in] and
