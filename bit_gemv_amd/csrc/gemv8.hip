@@ -202,17 +202,20 @@ static hipError_t launch8_rw(const WoArgs &a, hipStream_t st, int ks_count) {
 
 // Launch shape: four waves share k four ways at 4..7 chunks a row, two ways
 // at 2..3 or 8 and more, not at all for one chunk; 8 rows a wave when that
-// still leaves 512 blocks and the batch allows it. At batch 1 rows of 8 and
-// more chunks also split four ways, 4 rows a wave below 16 chunks (measured
-// on the 70B shapes, us per launch, two-way split -> four-way: 10240 x 8192
-// 19.9 -> 16.4, 8192 x 8192 15.7 -> 13.5, 57344 x 8192 80.9 -> 74.4,
-// 8192 x 28672 with 8 rows 43.4 -> 39.3).
+// still leaves 512 blocks and the batch allows it. At batch 1..3 rows of 8
+// and more chunks also split four ways: at batch 1 with 4 rows a wave below
+// 16 chunks (measured on the 70B shapes, us per launch, two-way split ->
+// four-way: 10240 x 8192 19.9 -> 16.4, 8192 x 8192 15.7 -> 13.5, 57344 x
+// 8192 80.9 -> 74.4, 8192 x 28672 with 8 rows 43.4 -> 39.3), at batch 2 and
+// 3 with 8 rows (batch 2: 22.6 -> 18.5, 16.4 -> 15.2, 85.2 -> 77.7,
+// 46.5 -> 43.0; batch 3: 2-11 % faster).
 template <int B, bool SYM>
 static hipError_t launch8(const WoArgs &a, hipStream_t st) {
     const int nchunks = (int)((a.k + kChunk8 - 1) / kChunk8);
-    if constexpr (B == 1) {
+    if constexpr (B <= 3) {
         if (nchunks >= 8) {
-            const bool rw8 = nchunks >= 16 && (a.n + 7) / 8 >= 512;
+            const bool tall = (a.n + 7) / 8 >= 512;
+            const bool rw8 = tall && (B > 1 || nchunks >= 16);
             return rw8 ? launch8_rw<B, 8, SYM>(a, st, 4) : launch8_rw<B, 4, SYM>(a, st, 4);
         }
     }

@@ -54,6 +54,15 @@ def test_batches_tall(b):
     _case(12288 + 7, 4096, b, False, seed=b + 40)
 
 
+@pytest.mark.parametrize("b", [2, 3])
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("n,k", [(4096 + 9, 8192 + 128), (300, 9216)])
+def test_small_batches_long_rows(n, k, b, sym):
+    """Batch 2 and 3 on rows of 8 and more chunks: the four-way k split,
+    with 8 rows a wave (4105 rows) and 4 (300 rows)."""
+    _case(n, k, b, sym, seed=b + n % 13)
+
+
 @pytest.mark.parametrize("b", [1, 6])
 @pytest.mark.parametrize("group,k", [(256, 4096), (384, 1152 * 3), (1024, 4096), ("k", 3072), ("k", 128)])
 def test_larger_groups(b, group, k):
