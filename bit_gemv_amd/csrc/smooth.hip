@@ -134,8 +134,9 @@ hipError_t launch_smooth_scale(const SmoothArgs &a, hipStream_t st) {
 constexpr int kTokLoads = 4;
 
 // Quotients x / smooth (IEEE division, as the definition) of elements
-// c0 + 8 t + 8 TPB i .. + 7 of the row; lanes past k produce zeros.
-template <int TPB, bool SM>
+// c0 + 8 t + 8 TPB i .. + 7 of the row; lanes past k produce zeros. FULL:
+// k is a whole number of chunks, so no lane is past k.
+template <int TPB, bool SM, bool FULL>
 LQ_DEVICE void token_chunk(const uint16_t *__restrict__ xr, const float *__restrict__ smooth, int64_t k, int64_t c0,
                            int t, float f[kTokLoads][8]) {
     u32x4 v[kTokLoads];
@@ -143,7 +144,7 @@ LQ_DEVICE void token_chunk(const uint16_t *__restrict__ xr, const float *__restr
 #pragma unroll
     for (int i = 0; i < kTokLoads; ++i) {
         const int64_t e = c0 + t * 8 + 8 * TPB * i;
-        const bool in = e < k;
+        const bool in = FULL || e < k;
         v[i] = in ? *reinterpret_cast<const u32x4 *>(xr + e) : u32x4{0u, 0u, 0u, 0u};
         if (SM) {
             const f32x4 one = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
@@ -164,7 +165,7 @@ LQ_DEVICE void token_chunk(const uint16_t *__restrict__ xr, const float *__restr
     }
 }
 
-template <int TPB, bool SM, bool ONE>
+template <int TPB, bool SM, bool ONE, bool FULL>
 __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__restrict__ x, int64_t k,
                                                            const float *__restrict__ smooth,
                                                            int8_t *__restrict__ qx, float *__restrict__ sx) {
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
     float f[kTokLoads][8];
     float a = 0.0f;
     for (int64_t ch = 0; ch < nch; ++ch) {
-        token_chunk<TPB, SM>(xr, smooth, k, ch * kTokChunk, t, f);
+        token_chunk<TPB, SM, FULL>(xr, smooth, k, ch * kTokChunk, t, f);
 #pragma unroll
         for (int i = 0; i < kTokLoads; ++i)
 #pragma unroll
@@ -200,11 +201,11 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
     const float y = 1.0f / s;
     // the last chunk is still in f; the others are read again
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
-        if (ch != nch - 1) token_chunk<TPB, SM>(xr, smooth, k, ch * kTokChunk, t, f);
+        if (ch != nch - 1) token_chunk<TPB, SM, FULL>(xr, smooth, k, ch * kTokChunk, t, f);
 #pragma unroll
         for (int i = 0; i < kTokLoads; ++i) {
             const int64_t e = ch * kTokChunk + t * 8 + 8 * TPB * i;
-            if (e >= k) continue;
+            if (!FULL && e >= k) continue;
             // q + 128 in 1 .. 255 is an exact small integer in a float:
             // v_cvt_pk_u8_f32 places its byte, and xor 0x80 turns q + 128
             // into the two's-complement byte of q
@@ -225,14 +226,19 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
 
 template <int TPB>
 static hipError_t launch_token_quant(const TokenQuantArgs &a, hipStream_t st) {
-    const bool one = a.k <= (int64_t)kTokLoads * TPB * 8;
-#define LQ_TQ(SM, ONE)                                                                                          \
-    if ((a.smooth != nullptr) == SM && one == ONE) {                                                            \
-        hipLaunchKernelGGL((token_quant_kernel<TPB, SM, ONE>), dim3((uint32_t)a.t), dim3(TPB), 0, st, a.x, a.k, \
-                           a.smooth, a.qx, a.sx);                                                               \
+    constexpr int64_t kChunkK = (int64_t)kTokLoads * TPB * 8;
+    const bool one = a.k <= kChunkK;
+    // whole chunks: no lane past k, so the loads and stores need no guard
+    // (512 x 8192 with smoothing: 7.7 -> 6.8 us)
+    const bool full = a.k % kChunkK == 0;
+#define LQ_TQ(SM, ONE, FULL)                                                                                    \
+    if ((a.smooth != nullptr) == SM && one == ONE && full == FULL) {                                            \
+        hipLaunchKernelGGL((token_quant_kernel<TPB, SM, ONE, FULL>), dim3((uint32_t)a.t), dim3(TPB), 0, st, a.x, \
+                           a.k, a.smooth, a.qx, a.sx);                                                          \
         return hipGetLastError();                                                                               \
     }
-    LQ_TQ(true, true) LQ_TQ(true, false) LQ_TQ(false, true) LQ_TQ(false, false)
+    LQ_TQ(true, true, true) LQ_TQ(true, false, true) LQ_TQ(false, true, true) LQ_TQ(false, false, true)
+    LQ_TQ(true, true, false) LQ_TQ(true, false, false) LQ_TQ(false, true, false) LQ_TQ(false, false, false)
 #undef LQ_TQ
     return hipErrorInvalidValue;
 }

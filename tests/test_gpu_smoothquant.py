@@ -68,7 +68,8 @@ def test_smooth_scale_zero_channels():
 # partial or full chunk, then 8320 and 28672 channels (two and four chunks,
 # the earlier ones read again for their codes).
 @pytest.mark.parametrize("smooth", [False, True])
-@pytest.mark.parametrize("t,k", [(1, 128), (5, 384), (64, 2048 + 128), (512, 8192), (3, 8192 + 128), (7, 28672)])
+@pytest.mark.parametrize("t,k", [(1, 128), (5, 384), (64, 2048 + 128), (512, 8192), (3, 8192 + 128), (7, 28672),
+                                 (4, 16384), (2, 65536)])
 def test_per_token_int8(t, k, smooth):
     x, w = _xw(t, 16, k, seed=k)
     sm = np.exp(np.random.default_rng(1).uniform(-2, 2, k)).astype(np.float32) if smooth else None
