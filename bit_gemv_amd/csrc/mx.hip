@@ -69,15 +69,19 @@ LQ_DEVICE uint32_t e2m1_codes8(const u32x4 v, int e) {
 // elements [32 b, 32 b + 32), code bytes [16 b, 16 b + 16) and scale byte b.
 constexpr int kMxChunks = 4;
 
-__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restrict__ w, int64_t total8,
-                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+// FULL: the block's chunks all exist (every block but the last), so its
+// loads and stores need no guard.
+template <bool FULL>
+LQ_DEVICE void mx_quant_body(const uint16_t *__restrict__ w, int64_t total8, uint8_t *__restrict__ codes,
+                             uint8_t *__restrict__ scales) {
     const int64_t base = (int64_t)blockIdx.x * (256 * kMxChunks) + threadIdx.x;
     u32x4 v[kMxChunks];
 #pragma unroll
     for (int c = 0; c < kMxChunks; ++c) {
         const int64_t i = base + 256 * c;
         // lanes past the end take part in the 4-lane maximum with zeros
-        v[c] = i < total8 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w) + i) : u32x4{0u, 0u, 0u, 0u};
+        v[c] = FULL || i < total8 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w) + i)
+                                  : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int c = 0; c < kMxChunks; ++c) {
@@ -91,11 +95,19 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restric
         a = fmaxf(a, dpp_move<kDppXor2>(a));
         const int e = mx_exponent(a);
         const uint32_t packed = e2m1_codes8(v[c], e);
-        if (i < total8) {
+        if (FULL || i < total8) {
             reinterpret_cast<uint32_t *>(codes)[i] = packed;
             if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t *__restrict__ w, int64_t total8,
+                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    if ((int64_t)(blockIdx.x + 1) * (256 * kMxChunks) <= total8)
+        mx_quant_body<true>(w, total8, codes, scales);
+    else
+        mx_quant_body<false>(w, total8, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
