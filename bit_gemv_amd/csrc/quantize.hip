@@ -569,31 +569,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                                                        float *__restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;
+    // both halves' code, scale and zero loads first (a lane past the end
+    // reads element 0 and stores nothing): 58.1 -> 55.6 us on 8192 x 8192
+    uint32_t v[2];
+    float s[2], z[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int64_t elem = base + 256 * h + 4 * lane;  // total is a multiple of 128
+        const int64_t e = elem < total ? elem : 0;
+        v[h] = BITS == 4 ? (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(codes + e / 2))
+                         : __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + e));
+        const int64_t g = e / group;  // groups tile the flattened matrix
+        s[h] = scales[g];
+        z[h] = SYM ? 0.0f : zeros[g];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t elem = base + 256 * h + 4 * lane;
         if (elem >= total) continue;
-        const int64_t g = elem / group;  // groups tile the flattened matrix
-        const float s = scales[g];
-        const float z = SYM ? 0.0f : zeros[g];
         int q[4];
-        if (BITS == 4) {
-            const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(codes + elem / 2));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int u = (int)((v >> (4 * j)) & 0xF);
+        for (int j = 0; j < 4; ++j) {
+            if (BITS == 4) {
+                const int u = (int)((v[h] >> (4 * j)) & 0xF);
                 q[j] = SYM ? u - 8 : u;
-            }
-        } else {
-            const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + elem));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t b = (v >> (8 * j)) & 0xFF;
+            } else {
+                const uint32_t b = (v[h] >> (8 * j)) & 0xFF;
                 q[j] = SYM ? (int)(int8_t)b : (int)b;
             }
         }
-        __builtin_nontemporal_store(f32x4{((float)q[0] - z) * s, ((float)q[1] - z) * s, ((float)q[2] - z) * s,
-                                          ((float)q[3] - z) * s},
+        __builtin_nontemporal_store(f32x4{((float)q[0] - z[h]) * s[h], ((float)q[1] - z[h]) * s[h],
+                                          ((float)q[2] - z[h]) * s[h], ((float)q[3] - z[h]) * s[h]},
                                     reinterpret_cast<f32x4 *>(out + elem));
     }
 }
