@@ -191,9 +191,26 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
         return kMx ? (uint32_t)(ws * 8 + 4 * w_ent) : (uint32_t)(((ws * kStageK + 128 * w_ent) / group) * 4);
     };
 
-    auto issue = [&](int st) {
-        uint8_t *slot = ring + (st % kShSlots) * kSlot;
-        const bool in = st < s1;
+    // Stages are visited in a rotated order: block b starts at window
+    // b mod (windows of its run) and wraps around, so that the blocks do not
+    // all read the same 128-byte column of their rows at once. INT4 and
+    // MXFP4 only (70B gate|up, one run: INT4 2-3 %, MXFP4 8-15 % faster);
+    // INT8 rows (k bytes apart rather than k / 2) measured 22 % slower with
+    // it. Runs whose length is not a whole number of windows keep the
+    // plain order. Slots and window buffers follow the visit index.
+    constexpr bool kRotate = !kInt8;
+    const int len = s1 - s0;
+    int rot = 0;
+    if (kRotate && len % kWinSt == 0 && len / kWinSt > 1) rot = (int)((blockIdx.x % (len / kWinSt)) * kWinSt);
+    auto phys = [&](int iv) -> int {  // visit index -> stage (iv < len)
+        int v = rot + iv;
+        if (v >= len) v -= len;
+        return s0 + v;
+    };
+    auto issue = [&](int iv) {
+        uint8_t *slot = ring + (iv % kShSlots) * kSlot;
+        const bool in = iv < len;
+        const int st = in ? phys(iv) : s1;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -206,8 +223,8 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
                 (__attribute__((address_space(3))) void *)(slot + (x_real[i] ? kXOff + 1024 * (kXPerWave * wave + i)
                                                                              : kDummy)),
                 16, in && x_real[i] ? x_off[i] + (uint32_t)st * kXRowBytes : kOutOfRange, 0, 0, 0);
-        if ((st - s0) % kWinSt == 0) {  // a window's first stage (wave-uniform)
-            uint8_t *win = ring + kWinOff + (((st - s0) / kWinSt) & 1) * kWinBuf;
+        if (iv % kWinSt == 0) {  // a window's first stage (wave-uniform)
+            uint8_t *win = ring + kWinOff + ((iv / kWinSt) & 1) * kWinBuf;
             const uint32_t word = win_word(st);
 #pragma unroll
             for (int i = 0; i < kWinLoads; ++i) {
@@ -249,19 +266,20 @@ __global__ __launch_bounds__(256) void gemv_shared_kernel(const uint16_t *__rest
             b_off[h][j] = kXOff + xrow * Fm::kXRowBytes + 16 * ((16 * h + 4 * kq + j) ^ xrow);
 
 #pragma unroll
-    for (int i = 0; i < kShSlots - 1; ++i) issue(s0 + i);
-    for (int st = s0; st < s1; ++st) {
+    for (int i = 0; i < kShSlots - 1; ++i) issue(i);
+    for (int iv = 0; iv < len; ++iv) {
+        const int st = phys(iv);
         // stage st has landed for every wave; the slot refilled below was
         // last read in the previous iteration, before this barrier
-        // (stage st + 1 carries a window's loads when it starts one)
-        if ((st + 1 - s0) % kWinSt == 0)
+        // (the next visited stage carries a window's loads when it starts one)
+        if ((iv + 1) % kWinSt == 0)
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm + kWinLoads) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
-        issue(st + kShSlots - 1);
-        const uint8_t *slot = ring + (st % kShSlots) * kSlot;
-        const int ws = st - (st - s0) % kWinSt;  // first stage of the window
-        const uint8_t *win = ring + kWinOff + (((st - s0) / kWinSt) & 1) * kWinBuf;
+        issue(iv + kShSlots - 1);
+        const uint8_t *slot = ring + (iv % kShSlots) * kSlot;
+        const int ws = st - iv % kWinSt;  // first stage of the window
+        const uint8_t *win = ring + kWinOff + ((iv / kWinSt) & 1) * kWinBuf;
 #pragma unroll
         for (int h = 0; h < Fm::kHalves; ++h) {
             // a half past the row's end (k a multiple of 128 only) is skipped:
