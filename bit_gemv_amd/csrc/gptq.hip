@@ -444,7 +444,10 @@ __global__ __launch_bounds__(256) void bf16_to_f32_kernel(const uint16_t *__rest
 // --------------------------------------------------------------------------
 constexpr int GB = 128;  // columns per block (the lazy batch)
 
-LQ_DEVICE float clampf_def(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+// The definition's clamp on a finite value (inputs are finite): v_med3, one
+// instruction in the serial per-column chain instead of two compares and two
+// selects.
+LQ_DEVICE float clampf_def(float v, float lo, float hi) { return __builtin_amdgcn_fmed3f(v, lo, hi); }
 
 template <int BITS, bool SYM>
 __global__ __launch_bounds__(1024) void gptq_block_kernel(float *__restrict__ w, int n, int k,
