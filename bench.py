@@ -637,6 +637,68 @@ def measure_c1_c2(dev) -> dict:
     return rows
 
 
+def measure_tp8_share(dev) -> dict:
+    """The 70B decode sweep at one GPU's share of 8-way tensor parallelism
+    (80 address-distinct layers from two content sets, asymmetric INT4 G=128,
+    batch 1): q|k|v 1280 x 8192, o 8192 x 1024, gate|up 7168 x 8192, down
+    8192 x 3584, against the read probe over the same buffers. The
+    all-reduce after o and down is not part of it (one GPU)."""
+    import numpy as np
+    import torch
+
+    import bit_gemv_amd as bg
+    from workloads import WORKLOADS, tp8_share_weights
+
+    wl = WORKLOADS["llama70b_decode"]
+    sym, group = wl.symmetric, wl.group
+
+    def dev_bf16(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    src = [[dev_bf16(m) for m in tp8_share_weights(wl, s_)] for s_ in range(2)]
+    shapes = [tuple(m.shape) for m in src[0]]
+    flats = [[None] * 4 for _ in range(wl.layers)]
+    packed = [[None] * 4 for _ in range(wl.layers)]
+    for layer in range(wl.layers):
+        for j, m in enumerate(src[layer % 2]):
+            flats[layer][j], packed[layer][j] = flat_packed(dev, shapes[j][0], shapes[j][1], 4, sym, group)
+            bg.quantize_groupwise(m, 4, sym, group, out=packed[layer][j])
+    del src
+    xs = {k_: dev_bf16(wl.activation(k_, 1)) for k_ in sorted({k_ for _, k_ in shapes})}
+    ys = [torch.empty((1, n_), dtype=torch.float32, device=dev) for n_, _ in shapes]
+
+    def sweep():
+        for layer in range(wl.layers):
+            for j, (n_, k_) in enumerate(shapes):
+                bg.w4a16_gemv(xs[k_], packed[layer][j], ys[j])
+
+    ms = _graph_ms(sweep, reps=10)
+    byt = wl.layers * sum(w4_bytes(n_, k_, 1, sym, group) for n_, k_ in shapes)
+    tbs = byt / (ms * 1e-3) / 1e12
+    sink = torch.empty(bg.load_library().lq_read_probe_sink_words(), dtype=torch.int32, device=dev)
+
+    def read_sweep():
+        for layer in range(wl.layers):
+            for j in range(4):
+                bg.hbm_read_probe(flats[layer][j], sink)
+
+    rs_ms = _graph_ms(read_sweep, reps=10)
+    read_bytes = wl.layers * sum(f.numel() for f in flats[0])
+    rs_tbs = read_bytes / (rs_ms * 1e-3) / 1e12
+    log(f"[bench] llama70b_decode 8-way share batch 1: {ms:.3f} ms/token, {tbs:.3f} TB/s "
+        f"(read probe {rs_ms:.3f} ms, {rs_tbs:.3f} TB/s)")
+    r = {"workload": "llama70b_decode, one GPU's 8-way tensor-parallel share", "layers": wl.layers,
+         "matrices": {nm: list(sh) for nm, sh in zip(["q|k|v", "o", "gate|up", "down"], shapes)},
+         "quant": "INT4 asym G=128, fp32 scale+zero", "batch": 1, "launches_per_token": wl.layers * 4,
+         "ms_per_token_step": round(ms, 4), "TBps": round(tbs, 4), "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4),
+         "bytes": byt, "hbm_read_ceiling": {"sweep_TBps": round(rs_tbs, 4), "sweep_ms_per_token": round(rs_ms, 4),
+                                            "batch1_over_probe_rate": round(tbs / rs_tbs, 4)},
+         "note": "the all-reduce of the o and down outputs between ranks is not measured (one GPU)"}
+    del packed, flats, xs, ys
+    torch.cuda.empty_cache()
+    return {"tp8_share_decode": r}
+
+
 # $REPO is the repository root; rocprofv3 runs from /tmp (export TMPDIR=/tmp)
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_kt -o kt -- "
              "python3 $REPO/bench.py --steps 5 --warmup 2 --skip-cpu")
@@ -1133,6 +1195,7 @@ def main() -> int:
 
     if not args.skip_rows:
         result["rows"].update(measure_c1_c2(dev))
+        result["rows"].update(measure_tp8_share(dev))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, B)

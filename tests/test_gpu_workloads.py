@@ -9,7 +9,7 @@ import torch
 import bit_gemv_amd as bg
 import oracle
 from gpu_helpers import assert_close, assert_same_bits, dev_bf16, host, say
-from workloads import WORKLOADS
+from workloads import WORKLOADS, tp8_share_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,28 @@ def test_llama70b_decode_layer(gi):
     wl = WORKLOADS["llama70b_decode"]
     _check_matrix(wl, 0, GROUPS[gi], [1, 4, 16], np.random.default_rng(70 + gi),
                   formats=("int4", "int8", "mxfp4"))
+
+
+@pytest.mark.parametrize("j", range(4))
+def test_llama70b_tp8_share(j):
+    """One GPU's share of an 8-way tensor-parallel 70B layer (the shapes the
+    benchmark's tp8_share_decode row times): codes of sampled rows bit-exact
+    and batch-1 outputs of those rows against the oracle."""
+    wl = WORKLOADS["llama70b_decode"]
+    w = tp8_share_weights(wl, 0)[j]
+    n, k = w.shape
+    say(f"tp8 share {n}x{k}")
+    pw = bg.quantize_groupwise(dev_bf16(w), 4, wl.symmetric, wl.group)
+    rows = np.sort(np.random.default_rng(80 + j).choice(n, 48, replace=False))
+    rows[0], rows[-1] = 0, n - 1
+    c_ref, s_ref, z_ref = oracle.quantize(w[rows], 4, wl.symmetric, wl.group)
+    assert_same_bits(_rows_of(pw.codes, rows), c_ref, "codes (sampled rows)")
+    assert_same_bits(_rows_of(pw.scales, rows), s_ref, "scales (sampled rows)")
+    assert_same_bits(_rows_of(pw.zeros, rows), z_ref, "zeros (sampled rows)")
+    x = wl.activation(k, 1)
+    y = host(bg.w4a16_gemv(dev_bf16(x), pw))
+    assert_close(y[:, rows], oracle.w4a16_matmul(x, c_ref, s_ref, z_ref, rows.size, k, wl.symmetric, wl.group),
+                 "y batch 1 (sampled rows)")
 
 
 @pytest.mark.parametrize("layer", [0, 31])

@@ -200,3 +200,24 @@ WORKLOADS = {
         notes="AWQ scale search: X 512 tokens with 41 channels x20, Llama-2-7B layer, asymmetric INT4 G=128"),
 }
 WORKLOAD_ORDER = ["single_4096", "llama7b_decode", "llama70b_decode", "prefill70b", "smoothquant"]
+
+
+def tp8_share_weights(wl, layer: int):
+    """One GPU's share (rank 0) of an 8-way tensor-parallel 70B layer, as
+    bf16 host arrays: q|k|v and gate|up split along n (the first eighth of
+    each of q, k, v, gate, up), o and down split along k on 128-aligned
+    group boundaries (the first eighth of their input channels)."""
+    names = [lin.name for lin in wl.linears]
+    idx = {nm: names.index(nm) for nm in names}
+
+    def head(nm):
+        lin = wl.linears[idx[nm]]
+        return wl.weight(layer, idx[nm], rows=np.arange(lin.n // 8))
+
+    qkv = np.concatenate([head("q"), head("k"), head("v")], 0)
+    gu = np.concatenate([head("gate"), head("up")], 0)
+    o = wl.weight(layer, idx["o"])
+    o = np.ascontiguousarray(o[:, : o.shape[1] // 8])
+    down = wl.weight(layer, idx["down"])
+    down = np.ascontiguousarray(down[:, : down.shape[1] // 8])
+    return [qkv, o, gu, down]
