@@ -161,7 +161,10 @@ lq_status w4a16_gemv(const void *x_bf16, int64_t b, const void *codes, const flo
  * scales  fp32 [n][k/group]; zeros fp32 [n][k/group] or NULL if symmetric.
  * y       out fp32 [b][n].
  * group: multiple of 128 dividing k; k multiple of 128 and at most 2^28.
- * Errors as w4a16_gemv; x, codes and y must be 16-byte aligned.
+ * Errors as w4a16_gemv; x, codes and y must be 16-byte aligned. Batch
+ * 4..16 on large matrices splits k as w4a16_gemv does (y zeroed on `stream`,
+ * partial sums added with float atomics; more than two runs: the last bits
+ * of y can vary from call to call).
  */
 lq_status w8a16_gemv(const void *x_bf16, int64_t b, const void *codes, const float *scales,
                      const float *zeros, int64_t n, int64_t k, int symmetric, int64_t group,
@@ -250,7 +253,10 @@ lq_status mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, void *codes, 
  *   y[i][r] = sum_j x[i][j] * E2M1(c[r][j]) * 2^(scales[r][j/32] - 127)
  * x_bf16 [b][k], b in 0..16 (larger: LQ_ERR_UNSUPPORTED); codes, scales as
  * mxfp4_quantize writes them; y out fp32 [b][n]. 16-byte aligned; k multiple
- * of 128 and at most 2^28.
+ * of 128 and at most 2^28. Batch 4..16 on large matrices splits k as
+ * w4a16_gemv does (y zeroed on `stream`, partial sums added with float
+ * atomics; more than two runs: the last bits of y can vary from call to
+ * call).
  */
 lq_status mxfp4_gemv(const void *x_bf16, int64_t b, const void *codes, const void *scales,
                      int64_t n, int64_t k, float *y, void *stream);
