@@ -206,21 +206,22 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
         for (int i = 0; i < kTokLoads; ++i) {
             const int64_t e = ch * kTokChunk + t * 8 + 8 * TPB * i;
             if (!FULL && e >= k) continue;
-            // q + 128 in 1 .. 255 is an exact small integer in a float:
-            // v_cvt_pk_u8_f32 places its byte, and xor 0x80 turns q + 128
-            // into the two's-complement byte of q
-            uint32_t lo = 0, hi = 0;
+            // Rounding, clamp and byte in one add. The clamp never binds:
+            // |X'| <= am and s = RN(am / 127) >= (am / 127)(1 - 2^-24), so
+            // |RN(X' / s)| <= 127 (1 + 2^-23) and rounds to at most 127.
+            // Floats in [2^23, 2^24) are the integers, so adding 2^23 + 256
+            // (even) rounds the quotient to an integer with ties to even,
+            // as rintf does, and leaves 256 + round(q), in 129 .. 383, in the
+            // low mantissa bits: its low byte is the two's-complement byte
+            // of round(q). Three byte permutes pack four of them.
+            uint32_t w[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // finite inputs: v_med3 is the clamp (one instruction
-                // instead of two compares and two selects)
-                const float q = __builtin_amdgcn_fmed3f(rintf(div_rn(f[i][j], s, y)), -127.0f, 127.0f) + 128.0f;
-                if (j < 4)
-                    lo = __builtin_amdgcn_cvt_pk_u8_f32(q, j, lo);
-                else
-                    hi = __builtin_amdgcn_cvt_pk_u8_f32(q, j - 4, hi);
-            }
-            *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo ^ 0x80808080u, hi ^ 0x80808080u};
+            for (int j = 0; j < 8; ++j) w[j] = __float_as_uint(div_rn(f[i][j], s, y) + 8388864.0f);
+            const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[3], w[2], 0x0C0C0400u),
+                                                      __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0400u), 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[7], w[6], 0x0C0C0400u),
+                                                      __builtin_amdgcn_perm(w[5], w[4], 0x0C0C0400u), 0x05040100u);
+            *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo, hi};
         }
     }
     if (t == 0) sx[row] = s;
