@@ -91,6 +91,38 @@ def test_per_token_edge_rows():
     assert_same_bits(host(sx), s_ref, "sx")
 
 
+@pytest.mark.parametrize("k", [256, 8192])
+def test_per_token_exact_ties_and_top_codes(k):
+    """Rows aimed at the code placement. Exact rounding ties: the
+    half-integers -126.5 .. 126.5 beside +-127, so s = 1 (and s = 2^-20 for
+    the row times 2^-20) and X' / s is m + 1/2 exactly, which must round to
+    the even neighbour. Rows whose scale s = RN(max|X'| / 127) rounded down,
+    so the top quotient max|X'| / s lies just above 127 and must still give
+    the code 127 (and -127 for its negative). 8192 channels (the 256 tiled)
+    take the kernel's unguarded whole-chunk form, 256 the guarded one."""
+    half = np.arange(-126.5, 127.0, 1.0)
+    tie = np.concatenate([[127.0, -127.0], half])
+    rows = [tie, tie * 2.0 ** -20]
+    rng = np.random.default_rng(41)
+    cand = oracle.bf16_bits_to_f32(f32_to_bf16_bits(rng.uniform(1e-3, 1e3, 4096)))
+    s32 = cand / np.float32(127.0)
+    down = cand[s32.astype(np.float64) < cand.astype(np.float64) / 127.0]
+    assert len(down) >= 14
+    for am in down[:14]:
+        rows.append(np.concatenate([[am, -am], am * rng.uniform(-1.0, 1.0, 254)]))
+    x = f32_to_bf16_bits(np.tile(np.stack(rows), (1, k // 256)))
+    for sm in (None, np.ones(k, np.float32)):
+        say(f"quant_per_token_int8 exact ties and top codes k={k} smooth={sm is not None}")
+        qx, sx = bg.quant_per_token_int8(dev_bf16(x), None if sm is None else dev(sm))
+        q_ref, s_ref = oracle.quant_per_token_int8(x, sm)
+        assert_same_bits(host(sx), s_ref, "sx")
+        assert_same_bits(host(qx), q_ref, "qx")
+    # what the rows are for, on the oracle's side
+    assert s_ref[0] == 1.0 and s_ref[1] == np.float32(2.0 ** -20)
+    assert (q_ref[:2, 2:256] == np.rint(half).astype(np.int8)).all()
+    assert (q_ref[:, 0] == 127).all() and (q_ref[:, 1] == -127).all()
+
+
 def test_per_token_quotients_next_to_rounding_ties():
     """Smoothed activations X' placed within 0..3 fp32 ulps of (m + 1/2) s,
     with s = max|X'| / 127 of the token, so X' / s lands next to (or on) a
