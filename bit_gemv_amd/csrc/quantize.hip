@@ -598,9 +598,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                 q[j] = SYM ? (int)(int8_t)b : (int)b;
             }
         }
-        __builtin_nontemporal_store(f32x4{((float)q[0] - z[h]) * s[h], ((float)q[1] - z[h]) * s[h],
-                                          ((float)q[2] - z[h]) * s[h], ((float)q[3] - z[h]) * s[h]},
-                                    reinterpret_cast<f32x4 *>(out + elem));
+        // plain stores: the non-temporal hint measured 3-5 % slower here
+        // (8192 x 8192 INT4 -> fp32, 55.5-58.3 against 52.9-55.1 us)
+        *reinterpret_cast<f32x4 *>(out + elem) = f32x4{((float)q[0] - z[h]) * s[h], ((float)q[1] - z[h]) * s[h],
+                                                       ((float)q[2] - z[h]) * s[h], ((float)q[3] - z[h]) * s[h]};
     }
 }
 
