@@ -135,8 +135,11 @@ constexpr int kTokLoads = 4;
 
 // Quotients x / smooth (IEEE division, as the definition) of elements
 // c0 + 8 t + 8 TPB i .. + 7 of the row; lanes past k produce zeros. FULL:
-// k is a whole number of chunks, so no lane is past k.
-template <int TPB, bool SM, bool FULL>
+// k is a whole number of chunks, so no lane is past k. NT: the row is one
+// chunk, read exactly once, so X comes with the streaming (non-temporal)
+// hint; rows of several chunks read the earlier ones again and keep the
+// default policy.
+template <int TPB, bool SM, bool FULL, bool NT>
 LQ_DEVICE void token_chunk(const uint16_t *__restrict__ xr, const float *__restrict__ smooth, int64_t k, int64_t c0,
                            int t, float f[kTokLoads][8]) {
     u32x4 v[kTokLoads];
@@ -145,7 +148,8 @@ LQ_DEVICE void token_chunk(const uint16_t *__restrict__ xr, const float *__restr
     for (int i = 0; i < kTokLoads; ++i) {
         const int64_t e = c0 + t * 8 + 8 * TPB * i;
         const bool in = FULL || e < k;
-        v[i] = in ? *reinterpret_cast<const u32x4 *>(xr + e) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(xr + e);
+        v[i] = !in ? u32x4{0u, 0u, 0u, 0u} : NT ? __builtin_nontemporal_load(p) : *p;
         if (SM) {
             const f32x4 one = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
             d[i][0] = in ? *reinterpret_cast<const f32x4 *>(smooth + e) : one;
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
     float f[kTokLoads][8];
     float a = 0.0f;
     for (int64_t ch = 0; ch < nch; ++ch) {
-        token_chunk<TPB, SM, FULL>(xr, smooth, k, ch * kTokChunk, t, f);
+        token_chunk<TPB, SM, FULL, ONE>(xr, smooth, k, ch * kTokChunk, t, f);
 #pragma unroll
         for (int i = 0; i < kTokLoads; ++i)
 #pragma unroll
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
     const float y = 1.0f / s;
     // the last chunk is still in f; the others are read again
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
-        if (ch != nch - 1) token_chunk<TPB, SM, FULL>(xr, smooth, k, ch * kTokChunk, t, f);
+        if (ch != nch - 1) token_chunk<TPB, SM, FULL, ONE>(xr, smooth, k, ch * kTokChunk, t, f);
 #pragma unroll
         for (int i = 0; i < kTokLoads; ++i) {
             const int64_t e = ch * kTokChunk + t * 8 + 8 * TPB * i;
@@ -221,7 +225,9 @@ __global__ __launch_bounds__(TPB) void token_quant_kernel(const uint16_t *__rest
                                                       __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0400u), 0x05040100u);
             const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[7], w[6], 0x0C0C0400u),
                                                       __builtin_amdgcn_perm(w[5], w[4], 0x0C0C0400u), 0x05040100u);
-            *reinterpret_cast<u32x2 *>(qx + row * k + e) = u32x2{lo, hi};
+            // codes are written once: streaming stores (with the streaming
+            // loads of one-chunk rows, 512 x 8192: 6.28-6.37 -> 5.83-5.90 us)
+            __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(qx + row * k + e));
         }
     }
     if (t == 0) sx[row] = s;
