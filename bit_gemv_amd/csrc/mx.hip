@@ -96,7 +96,9 @@ LQ_DEVICE void mx_quant_body(const uint16_t *__restrict__ w, int64_t total8, uin
         const int e = mx_exponent(a);
         const uint32_t packed = e2m1_codes8(v[c], e);
         if (FULL || i < total8) {
-            reinterpret_cast<uint32_t *>(codes)[i] = packed;
+            // streaming code stores (written once): 70B stack 5.87-5.90 ->
+            // 5.56-5.59 ms; the hint on the scale bytes as well measured slower
+            __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(codes) + i);
             if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
         }
     }
